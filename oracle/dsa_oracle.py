@@ -1,0 +1,295 @@
+"""CPU oracle of the DeepSeek Sparse Attention (DSA) hot path — TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, fp64 NumPy.  It exists to check the HIP library; only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import it.
+The product path (``sparse_attention_long_gemm_amd``) never imports, calls or links it, and it
+shares no code with that path: its FP8/bf16 decoders, scoring, selection and attention are all
+written here from the definitions below.
+
+What the path computes (one query row t of a causal sequence; decode is the same with
+t = ctx - 1 and keys read through a page table):
+
+1. Lightning-indexer score, for every earlier key s <= t:
+       I[t, s] = sum_j  w[t, j] * ReLU( q_I[t, j, :] . k_I[s, :] )
+   a ReLU-activated dot product per indexer head, weighted and summed over a handful of
+   heads, with FP8 operands.  Sources: jdon.com "DeepSeek-V3.2-Exp" article, paragraph on the
+   lightning indexer (ReLU, weight w_I, q_I meeting k_I, few heads H_I, FP8); openi.cn
+   "DeepSeek-V3.2" page, section on the technology behind the model (the indexer relates the
+   query token to the preceding tokens).  The keys are shared by all indexer heads.
+2. Fine-grained token selection: keep the k = 2048 keys of highest score, drop the rest
+   (jdon.com article, paragraph on fine-grained token selection; openi.cn page, item on token
+   selection).  Ties are broken toward the lower position; with n = min(k, t + 1) candidates
+   the selection is unique.  Scores are compared numerically (-0 == +0).
+3. Attention in MQA mode over only the selected entries: one shared latent KV row per token
+   (K = all D_k dims, V = its first D_v dims) serves every query head (openi.cn page, item on
+   MLA in MQA mode; mundobytes.com page, section "How it works: lightning indexer and token
+   selection").  o[t, h] = sum_s softmax_s(scale * q[t, h] . kv[s]) * kv[s, :D_v] and
+   lse[t, h] = log sum_s exp(scale * q[t, h] . kv[s]) over the selected s.
+
+Readings where the pages are silent (listed with reasons in the design notes): the key at
+s = t itself is a candidate; ties go to the lowest index; FP8 is OCP e4m3fn with no scale
+factors; the softmax scale is 1/sqrt(D_k); an empty selection gives o = 0 and lse = -inf;
+a selected index that is -1 or outside [0, t] contributes nothing.
+
+Exactness: operands on the dyadic grids the tests use make every score exact in fp64 (and in
+fp32), so the selection is decided identically on both sides.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------------------
+
+
+def _e4m3fn_table() -> np.ndarray:
+    """All 256 OCP e4m3fn codes as fp64: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+
+    Exponent field 0 is subnormal (m/8 * 2^-6); the single NaN pattern per sign is
+    exponent 15 with mantissa 7; there are no infinities (largest finite value 448).
+    """
+    tab = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            tab[code] = np.nan
+        elif e == 0:
+            tab[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            tab[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return tab
+
+
+E4M3FN = _e4m3fn_table()
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """FP8 e4m3fn bytes (uint8 array / tensor) -> exact fp64 values."""
+    c = _np(codes).astype(np.uint8)
+    return E4M3FN[c]
+
+
+def decode_bf16(x) -> np.ndarray:
+    """bf16 values (torch.bfloat16 tensor, or their uint16 bit patterns) -> exact fp64.
+
+    A bf16 number is the upper half of an fp32 bit pattern, so widening is a 16-bit shift.
+    """
+    u = _np(x).view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _np(x) -> np.ndarray:
+    """Host NumPy view of an array or tensor; bf16 tensors come back as their uint16 bits."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach()
+            if x.dtype == torch.bfloat16:
+                x = x.view(torch.int16)
+            return x.cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x)
+
+
+# ----------------------------------------------------------------------------------------
+# Step 1: lightning-indexer scores
+# ----------------------------------------------------------------------------------------
+
+
+def indexer_scores(q_i: np.ndarray, w: np.ndarray, k_i: np.ndarray) -> np.ndarray:
+    """Scores of one query row against the candidate keys.
+
+    q_i: [H_I, d_I] fp64, w: [H_I] fp64, k_i: [n, d_I] fp64 (the keys s = 0..n-1, n = t + 1).
+    Returns I: [n] with I[s] = sum_j w[j] * max(q_i[j] . k_i[s], 0).
+    (jdon.com article, lightning-indexer paragraph.)
+    """
+    x = k_i @ q_i.T                      # [n, H_I]: per-head dot products q_I[j] . k_I[s]
+    relu = np.maximum(x, 0.0)            # ReLU activation per head
+    scores = relu @ w                    # weighted sum over indexer heads
+    return scores + 0.0                  # -0 -> +0, so equal scores compare equal
+
+
+# ----------------------------------------------------------------------------------------
+# Step 2: top-k selection
+# ----------------------------------------------------------------------------------------
+
+
+def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k best keys under (score descending, index ascending); int32 [k].
+
+    n = min(k, len(scores)) indices are returned in ascending order, then -1 padding.
+    (jdon.com article, paragraph on fine-grained token selection: keep the 2048 highest.)
+    """
+    n = scores.shape[0]
+    pos = np.arange(n)
+    order = np.lexsort((pos, -scores))   # primary key: -score; secondary: position
+    m = min(k, n)
+    sel = np.sort(order[:m]).astype(np.int32)
+    out = np.full(k, -1, dtype=np.int32)
+    out[:m] = sel
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Step 3: sparse MQA attention over the selected shared KV rows
+# ----------------------------------------------------------------------------------------
+
+
+def sparse_mqa(q: np.ndarray, kv_sel: np.ndarray, d_v: int, scale: float):
+    """Attention of every head of one query over the selected shared rows.
+
+    q: [H, D_k] fp64; kv_sel: [m, D_k] fp64 (the selected rows; V is the first d_v dims).
+    Returns (o [H, d_v], lse [H]); with m == 0, o = 0 and lse = -inf.
+    (openi.cn page: MQA mode, one KV entry shared by many queries; only the top-k entries
+    are attended.)
+    """
+    H = q.shape[0]
+    if kv_sel.shape[0] == 0:
+        return np.zeros((H, d_v)), np.full(H, -np.inf)
+    z = scale * (q @ kv_sel.T)                       # [H, m] logits
+    zmax = z.max(axis=1, keepdims=True)
+    p = np.exp(z - zmax)
+    den = p.sum(axis=1, keepdims=True)
+    o = (p @ kv_sel[:, :d_v]) / den
+    lse = (zmax + np.log(den))[:, 0]
+    return o, lse
+
+
+def valid_selected(idx_row: np.ndarray, t: int) -> np.ndarray:
+    """The entries of an index row that are attended: in [0, t]; -1 and others are skipped."""
+    return idx_row[(idx_row >= 0) & (idx_row <= t)]
+
+
+# ----------------------------------------------------------------------------------------
+# Whole-path drivers (prefill of one contiguous sequence; paged decode)
+# ----------------------------------------------------------------------------------------
+
+
+def prefill_indexer_topk(inp: dict, rows=None) -> np.ndarray:
+    """Top-k index rows for the given query rows (local row numbers; default all)."""
+    q_i = decode_e4m3fn(inp["q_idx"])
+    k_i = decode_e4m3fn(inp["k_idx"])
+    w = _np(inp["w"]).astype(np.float64)
+    q_pos = _np(inp["q_pos"]).astype(np.int64)
+    k = int(inp["top_k"])
+    rows = range(q_pos.shape[0]) if rows is None else rows
+    out = np.empty((len(rows), k), dtype=np.int32)
+    for r, i in enumerate(rows):
+        t = int(q_pos[i])
+        sc = indexer_scores(q_i[i], w[i], k_i[: t + 1])
+        out[r] = topk_select(sc, k)
+    return out
+
+
+def prefill(inp: dict, rows=None, idx=None):
+    """Full path for the given rows: returns (idx [n,k], o [n,H,D_v], lse [n,H]).
+
+    ``idx`` may be passed to run step 3 on a given selection (the selection itself is then
+    not recomputed).
+    """
+    rows = list(range(_np(inp["q_pos"]).shape[0])) if rows is None else list(rows)
+    if idx is None:
+        idx = prefill_indexer_topk(inp, rows)
+    q_pos = _np(inp["q_pos"]).astype(np.int64)
+    kv_bits = _np(inp["kv"])                  # raw bf16 bits, decoded per gathered set
+    d_v = int(inp["D_v"])
+    scale = float(inp["scale"])
+    qt = inp["q"]
+    H = qt.shape[1]
+    o = np.empty((len(rows), H, d_v))
+    lse = np.empty((len(rows), H))
+    for r, i in enumerate(rows):
+        t = int(q_pos[i])
+        sel = valid_selected(np.asarray(idx[r]), t)
+        q = decode_bf16(qt[i])
+        o[r], lse[r] = sparse_mqa(q, decode_bf16(kv_bits[sel]), d_v, scale)
+    return idx, o, lse
+
+
+def paged_rows(cache, page_table_row, n: int, page_size: int) -> np.ndarray:
+    """Logical rows 0..n-1 of one sequence from a paged cache (host copy; bf16 as uint16 bits).
+
+    Row s lives at page page_table_row[s // page_size], slot s % page_size.  Paging with
+    page size 64 is the serving layout named on the mundobytes.com page (section "Quick guide
+    to running locally") and used by the paged indexer kernels it mentions (section "Open
+    kernels and ecosystem support").
+    """
+    pt = _np(page_table_row).astype(np.int64)
+    s = np.arange(n)
+    pages, slots = pt[s // page_size], s % page_size
+    try:
+        import torch
+        if isinstance(cache, torch.Tensor):     # gather on the tensor's device, copy n rows
+            dev = cache.device
+            rows = cache[torch.as_tensor(pages, device=dev), torch.as_tensor(slots, device=dev)]
+            return _np(rows)
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(cache)[pages, slots]
+
+
+def decode(inp: dict, seqs=None, idx=None):
+    """One paged decode step: per sequence b, query at t = ctx_b - 1 over keys [0, ctx_b).
+
+    Returns (idx [B,k], o [B,H,D_v], lse [B,H]) for the requested sequences.
+    """
+    ctx = _np(inp["ctx"]).astype(np.int64)
+    pt = _np(inp["page_table"])
+    P = int(inp["page_size"])
+    k = int(inp["top_k"])
+    d_v = int(inp["D_v"])
+    scale = float(inp["scale"])
+    seqs = list(range(ctx.shape[0])) if seqs is None else list(seqs)
+    q_i_all = decode_e4m3fn(inp["q_idx"])
+    w_all = _np(inp["w"]).astype(np.float64)
+    kc = inp["k_cache"]
+    kvc = inp["kv_cache"]
+    H = inp["q"].shape[1]
+    out_idx = np.empty((len(seqs), k), dtype=np.int32)
+    o = np.empty((len(seqs), H, d_v))
+    lse = np.empty((len(seqs), H))
+    for r, b in enumerate(seqs):
+        n = int(ctx[b])
+        t = n - 1
+        if idx is None:
+            k_i = decode_e4m3fn(paged_rows(kc, pt[b], n, P))
+            sc = indexer_scores(q_i_all[b], w_all[b], k_i)
+            out_idx[r] = topk_select(sc, k)
+        else:
+            out_idx[r] = np.asarray(idx[r])
+        sel = valid_selected(out_idx[r], t)
+        kv_bits = paged_rows(kvc, pt[b], n, P)
+        q = decode_bf16(inp["q"][b])
+        o[r], lse[r] = sparse_mqa(q, decode_bf16(kv_bits[sel]), d_v, scale)
+    return out_idx, o, lse
+
+
+# ----------------------------------------------------------------------------------------
+# Work model used to extrapolate sampled oracle timings
+# ----------------------------------------------------------------------------------------
+
+
+def row_work(t: int, H_I: int, d_I: int, H: int, D_k: int, D_v: int, k: int) -> float:
+    """Multiply-adds x2 that one prefill row t costs: indexer over t+1 keys + MQA over min(k,t+1)."""
+    return (t + 1) * 2.0 * H_I * d_I + min(k, t + 1) * 2.0 * H * (D_k + D_v)
+
+
+def causal_pairs(L: int) -> int:
+    return L * (L + 1) // 2
+
+
+def selected_pairs(L: int, k: int) -> int:
+    """Sum over t < L of min(k, t + 1)."""
+    m = min(k, L)
+    return m * (m + 1) // 2 + max(0, L - k) * k
+
+
+__all__ = [
+    "E4M3FN", "decode_e4m3fn", "decode_bf16", "indexer_scores", "topk_select", "sparse_mqa",
+    "valid_selected", "prefill_indexer_topk", "prefill", "paged_rows", "decode", "row_work",
+    "causal_pairs", "selected_pairs",
+]

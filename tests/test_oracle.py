@@ -1,0 +1,383 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped ReLU or weight, a wrong
+sign, a transposed operand, the wrong tie-break, an off-by-one causal bound, K and V swapped)
+fails at least one of them; ``test_planted_mistakes_are_caught`` plants such slips and checks.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gen import inputs as gi
+from oracle import brute
+from oracle import dsa_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------- number formats
+
+def test_e4m3fn_table_matches_torch_cast():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = orc.decode_e4m3fn(codes)
+    nan_ref, nan_mine = np.isnan(ref), np.isnan(mine)
+    assert (nan_ref == nan_mine).all()
+    assert nan_mine.sum() == 2                      # 0x7F and 0xFF
+    assert np.array_equal(ref[~nan_ref], mine[~nan_mine])
+    assert orc.decode_e4m3fn(np.array([0x7E]))[0] == 448.0
+    assert orc.decode_e4m3fn(np.array([0x01]))[0] == 2.0 ** -9
+
+
+def test_e4m3fn_brute_field_decoder_agrees():
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            continue
+        assert float(brute.e4m3fn_value(c)) == orc.E4M3FN[c]
+
+
+def test_bf16_decode_matches_torch():
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(4096, generator=g) * torch.exp(torch.randn(4096, generator=g) * 10)
+    xb = x.to(torch.bfloat16)
+    ref = xb.to(torch.float64).numpy()
+    assert np.array_equal(orc.decode_bf16(xb), ref)
+    bits = xb.view(torch.int16).numpy()
+    assert all(brute.bf16_value(int(b) & 0xFFFF) == r for b, r in zip(bits[:64], ref[:64]))
+
+
+# --------------------------------------------------------------------------- step 1: scores
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_scores_handworked_example():
+    g = _golden("indexer_handworked.json")
+    sc = orc.indexer_scores(np.array(g["q_I"]), np.array(g["w"]), np.array(g["k_I"])[: g["t"] + 1])
+    assert sc.tolist() == g["scores"]
+    for k, want in g["topk"].items():
+        assert orc.topk_select(sc, int(k)).tolist() == want
+
+
+def _tiny_grid(seed, L=48, H_I=3, d_I=8, lo=-3, hi=3, w=(0.25, 0.5, 1.0, -0.5)):
+    q = gi.grid_fp8((H_I, d_I), lo, hi, 0.125, seed, 101)
+    k = gi.grid_fp8((L, d_I), lo, hi, 0.125, seed, 102)
+    ww = gi.choice_f32((H_I,), w, seed, 103)
+    return q, k, ww
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_scores_equal_exact_rational_brute_force(seed):
+    q, k, w = _tiny_grid(seed)
+    t = 40
+    mine = orc.indexer_scores(orc.decode_e4m3fn(q), w.numpy().astype(np.float64),
+                              orc.decode_e4m3fn(k)[: t + 1])
+    exact = brute.scores(q.tolist(), w.tolist(), k.tolist(), t)
+    assert [float(x) for x in exact] == mine.tolist()      # exact on the dyadic grid
+
+
+def test_scores_single_head_unit_weight_is_relu_of_matmul():
+    q, k, _ = _tiny_grid(11, H_I=1)
+    qf = q.view(torch.float8_e4m3fn).to(torch.float64)
+    kf = k.view(torch.float8_e4m3fn).to(torch.float64)
+    ref = torch.relu(kf @ qf[0]).numpy()
+    mine = orc.indexer_scores(orc.decode_e4m3fn(q), np.ones(1), orc.decode_e4m3fn(k))
+    assert np.array_equal(mine, ref)
+
+
+def test_scores_weighted_heads_match_library_einsum():
+    q, k, w = _tiny_grid(12, H_I=5, d_I=16)
+    qf = q.view(torch.float8_e4m3fn).to(torch.float64)
+    kf = k.view(torch.float8_e4m3fn).to(torch.float64)
+    ref = (torch.relu(torch.einsum("jd,sd->sj", qf, kf)) * w.to(torch.float64)).sum(1).numpy()
+    mine = orc.indexer_scores(orc.decode_e4m3fn(q), w.numpy().astype(np.float64), orc.decode_e4m3fn(k))
+    assert np.array_equal(mine, ref)
+
+
+def test_scores_are_exact_in_fp32_on_production_grid():
+    """Dyadic grid {-2..2}/8, w in 2^{-4..0}, d_I=128, H_I=64: every score is a multiple of
+    2^-10 of magnitude <= 512, hence fp32-exact in any summation order."""
+    wl = gi.indexer_workload()
+    d = gi.prefill_inputs(gi.Workload(name="x", L=600, idx=wl.idx, mqa=None))
+    qi, ki = orc.decode_e4m3fn(d["q_idx"]), orc.decode_e4m3fn(d["k_idx"])
+    w = d["w"].numpy().astype(np.float64)
+    for t in (0, 17, 599):
+        sc = orc.indexer_scores(qi[t], w[t], ki[: t + 1])
+        assert np.all(sc * 1024 == np.round(sc * 1024)) and np.all(np.abs(sc) <= 512)
+        assert np.array_equal(sc.astype(np.float32).astype(np.float64), sc)
+        # a reversed-order fp32 sum gives the same values
+        x = (ki[: t + 1] @ qi[t].T).astype(np.float32)
+        acc = np.zeros(t + 1, dtype=np.float32)
+        for j in reversed(range(qi.shape[1])):
+            acc += np.float32(w[t, j]) * np.maximum(x[:, j], np.float32(0))
+        assert np.array_equal(acc.astype(np.float64), sc)
+
+
+# --------------------------------------------------------------------------- step 2: top-k
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("k", [1, 3, 7, 20, 64])
+def test_topk_equals_counting_definition(seed, k):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 40))
+    sc = rng.integers(-3, 4, n).astype(np.float64) * 0.5     # many ties
+    sc[rng.random(n) < 0.2] = -0.0                           # signed zeros tie with +0
+    want = brute.topk(sc.tolist(), k)
+    got = orc.topk_select(sc, k)
+    assert got[: len(want)].tolist() == want
+    assert (got[len(want):] == -1).all()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    n, k = 500, 37
+    sc = rng.integers(0, 30, n).astype(np.float64)
+    sel = orc.topk_select(sc, k)
+    assert (sel[: min(k, n)] >= 0).all() and len(set(sel.tolist())) == k
+    mask = np.zeros(n, bool)
+    mask[sel] = True
+    assert sc[mask].min() >= sc[~mask].max()
+    thr = sc[mask].min()
+    tied = np.flatnonzero(sc == thr)
+    kept_tied = np.flatnonzero(mask & (sc == thr))
+    assert kept_tied.tolist() == tied[: len(kept_tied)].tolist()      # lowest positions win
+    # nesting: the top-k is contained in the top-(k+10)
+    assert set(sel.tolist()) <= set(orc.topk_select(sc, k + 10).tolist())
+    # fewer candidates than k: all of them, then -1
+    few = orc.topk_select(sc[:5], k)
+    assert few[:5].tolist() == [0, 1, 2, 3, 4] and (few[5:] == -1).all()
+
+
+def test_zero_query_gives_first_positions():
+    """q_I = 0 makes every score 0, so the selection is positions 0..n-1 (closed form)."""
+    d = gi.prefill_inputs(gi.tiny_workload(), with_mqa=False)
+    d["q_idx"] = torch.zeros_like(d["q_idx"])
+    idx = orc.prefill_indexer_topk(d, rows=[0, 5, 31, 32, 255])
+    for r, t in enumerate([0, 5, 31, 32, 255]):
+        n = min(32, t + 1)
+        assert idx[r, :n].tolist() == list(range(n)) and (idx[r, n:] == -1).all()
+
+
+# --------------------------------------------------------------------------- step 3: attention
+
+def test_attention_handworked_example():
+    g = _golden("attention_handworked.json")
+    kv = np.array([[4.0, 0.0], [8.0, math.log(3.0)]])
+    o, lse = orc.sparse_mqa(np.array(g["q"]), kv, g["d_v"], g["scale"])
+    assert abs(o[0, 0] - 7.0) < 1e-12 and abs(lse[0] - math.log(4.0)) < 1e-12
+
+
+@pytest.mark.parametrize("D_k,D_v", [(64, 64), (96, 64)])
+def test_full_selection_equals_dense_causal_sdpa(D_k, D_v):
+    """With k >= t + 1 every earlier key is selected, so DSA is dense causal attention."""
+    L, H = 40, 3
+    wl = gi.Workload(name="t", L=L,
+                     idx=gi.IndexerSpec(H_I=2, d_I=16, grid_lo=-3, grid_hi=3, grid_step=0.125,
+                                        w_choices=(0.5, 1.0), top_k=L),
+                     mqa=gi.MqaSpec(H=H, D_k=D_k, D_v=D_v, sigma=1.0, scale=D_k ** -0.5))
+    d = gi.prefill_inputs(wl)
+    idx, o, lse = orc.prefill(d)
+    assert (idx[np.arange(L), np.arange(L)] == np.arange(L)).all()   # diagonal: s = t kept
+    q = d["q"].to(torch.float64).permute(1, 0, 2)                      # [H, L, D_k]
+    kv = d["kv"].to(torch.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, kv[None, :, :].expand(H, L, D_k).contiguous(),
+        kv[None, :, :D_v].expand(H, L, D_v).contiguous(), is_causal=True, scale=D_k ** -0.5)
+    assert np.allclose(o, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    zz = torch.einsum("hld,sd->hls", q, kv) * D_k ** -0.5
+    zz = zz.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), -math.inf)
+    assert np.allclose(lse, torch.logsumexp(zz, -1).T.numpy(), rtol=0, atol=1e-12)
+
+
+def test_sparse_attention_equals_brute_masked_dense_attention():
+    wl = gi.tiny_workload()
+    wl.L = 80
+    d = gi.prefill_inputs(wl)
+    rows = [0, 10, 31, 32, 50, 79]
+    idx, o, lse = orc.prefill(d, rows=rows)
+    qb = d["q"].view(torch.int16).numpy()
+    kvb = d["kv"].view(torch.int16).numpy()
+    kv_rows = [[brute.bf16_value(int(x)) for x in r] for r in kvb]
+    for r, t in enumerate(rows):
+        keep = brute.topk(brute.scores(d["q_idx"][t].tolist(), d["w"][t].tolist(),
+                                       d["k_idx"].tolist(), t), 32)
+        assert idx[r][idx[r] >= 0].tolist() == keep
+        qr = [[brute.bf16_value(int(x)) for x in hrow] for hrow in qb[t]]
+        bo, bl = brute.masked_attention(qr, kv_rows, t, keep, 64, 1 / 8)
+        assert np.allclose(o[r], np.array(bo), rtol=0, atol=1e-12)
+        assert np.allclose(lse[r], np.array(bl), rtol=0, atol=1e-12)
+
+
+def test_attention_invariants():
+    rng = np.random.default_rng(3)
+    H, m, D_k, D_v = 4, 30, 24, 16
+    q = rng.standard_normal((H, D_k))
+    kv = rng.standard_normal((m, D_k))
+    o, lse = orc.sparse_mqa(q, kv, D_v, 0.3)
+    # permutation of the selected rows changes nothing (to rounding)
+    perm = rng.permutation(m)
+    o2, lse2 = orc.sparse_mqa(q, kv[perm], D_v, 0.3)
+    assert np.allclose(o, o2, atol=1e-13) and np.allclose(lse, lse2, atol=1e-13)
+    # probabilities sum to one: sum_s exp(z_s - lse) == 1
+    z = 0.3 * q @ kv.T
+    assert np.allclose(np.exp(z - lse[:, None]).sum(1), 1.0, atol=1e-13)
+    # constant V rows give that constant
+    kvc = kv.copy()
+    kvc[:, :D_v] = 2.5
+    oc, _ = orc.sparse_mqa(q, kvc, D_v, 0.3)
+    assert np.allclose(oc, 2.5, atol=1e-13)
+    # one dominant logit picks that row's V
+    kvd = kv.copy()
+    kvd[7, D_v:] = 200.0 * np.sign(q[0, D_v:])
+    od, _ = orc.sparse_mqa(q[:1], kvd, D_v, 1.0)
+    assert np.allclose(od[0], kvd[7, :D_v], atol=1e-9)
+    # empty selection
+    oe, le = orc.sparse_mqa(q, kv[:0], D_v, 0.3)
+    assert (oe == 0).all() and np.isneginf(le).all()
+
+
+def test_invalid_indices_are_skipped():
+    d = gi.prefill_inputs(gi.tiny_workload())
+    idx, o, lse = orc.prefill(d, rows=[40])
+    bad = idx.copy()
+    bad[0, 5] = -1            # drop one entry
+    bad[0, 6] = 41            # beyond t = 40: ignored
+    _, o2, _ = orc.prefill(d, rows=[40], idx=bad)
+    keep = [s for s in idx[0].tolist() if s not in (idx[0, 5], idx[0, 6])]
+    _, o3, _ = orc.prefill(d, rows=[40], idx=np.array([keep + [-1] * (32 - len(keep))]))
+    assert np.allclose(o2, o3, atol=0)
+
+
+# --------------------------------------------------------------------------- decode
+
+def _tiny_decode(seed, page_size=16, ctx=(37, 100, 64, 1)):
+    sp = gi.DecodeSpec(B=len(ctx), page_size=page_size, spare_pages=3,
+                       idx=gi.IndexerSpec(H_I=4, d_I=32, grid_lo=-3, grid_hi=3, grid_step=0.125,
+                                          w_choices=(0.25, 0.5, 1.0), top_k=32),
+                       mqa=gi.MqaSpec(H=8, D_k=96, D_v=64, sigma=1.0, scale=96 ** -0.5))
+    return gi.decode_inputs(sp, seed=seed, ctx_lens=ctx)
+
+
+def test_decode_equals_prefill_last_row():
+    d = _tiny_decode(0)
+    idx, o, lse = orc.decode(d)
+    P = d["page_size"]
+    for b, n in enumerate(d["ctx"].tolist()):
+        pt = d["page_table"][b]
+        s = torch.arange(n)
+        k_rows = d["k_cache"][pt[s // P].long(), s % P]
+        kv_rows = d["kv_cache"][pt[s // P].long(), s % P]
+        pre = {"q_idx": d["q_idx"][b:b + 1], "w": d["w"][b:b + 1], "k_idx": k_rows,
+               "q_pos": torch.tensor([n - 1], dtype=torch.int32), "top_k": d["top_k"],
+               "q": d["q"][b:b + 1], "kv": kv_rows, "D_v": d["D_v"], "scale": d["scale"]}
+        i2, o2, l2 = orc.prefill(pre)
+        assert np.array_equal(i2[0], idx[b])
+        assert np.allclose(o2[0], o[b], atol=1e-13) and np.allclose(l2[0], lse[b], atol=1e-13)
+
+
+def test_decode_invariant_under_page_permutation():
+    d = _tiny_decode(1)
+    idx, o, lse = orc.decode(d)
+    ctx = d["ctx"].tolist()
+    pt_id, n_used = gi.identity_page_table(ctx, d["page_size"])
+    kc = torch.zeros((n_used,) + tuple(d["k_cache"].shape[1:]), dtype=torch.uint8)
+    kvc = torch.zeros((n_used,) + tuple(d["kv_cache"].shape[1:]), dtype=torch.bfloat16)
+    P = d["page_size"]
+    for b, n in enumerate(ctx):
+        s = torch.arange(n)
+        src = d["page_table"][b][s // P].long()
+        kc[pt_id[b][s // P].long(), s % P] = d["k_cache"][src, s % P]
+        kvc[pt_id[b][s // P].long(), s % P] = d["kv_cache"][src, s % P]
+    d2 = dict(d, page_table=pt_id, k_cache=kc, kv_cache=kvc, n_pages=n_used)
+    i2, o2, l2 = orc.decode(d2)
+    assert np.array_equal(idx, i2) and np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+# --------------------------------------------------------------------------- generators
+
+def test_generators_are_seeded_and_on_grid():
+    a = gi.prefill_inputs(gi.tiny_workload())
+    b = gi.prefill_inputs(gi.tiny_workload())
+    c = gi.prefill_inputs(gi.tiny_workload(), seed=1)
+    for key in ("q_idx", "w", "k_idx", "q", "kv"):
+        assert torch.equal(a[key], b[key])
+        assert not torch.equal(a[key], c[key])
+    vals = orc.decode_e4m3fn(a["q_idx"]) * 8
+    assert set(np.unique(vals).tolist()) <= set(range(-3, 4))
+    assert set(np.unique(a["w"].numpy()).tolist()) <= {0.25, 0.5, 1.0}
+    part = gi.prefill_inputs(gi.tiny_workload(), rows=(100, 7))
+    assert torch.equal(part["q_idx"], a["q_idx"][100:107]) and torch.equal(part["q"], a["q"][100:107])
+
+
+def test_work_model_closed_forms():
+    assert orc.causal_pairs(131072) == 8_590_000_128
+    assert orc.selected_pairs(131072, 2048) == sum(min(2048, t + 1) for t in range(131072))
+    assert orc.selected_pairs(100, 2048) == 5050
+
+
+# --------------------------------------------------------------------------- planted mistakes
+
+def _pins_pass(monkeypatched):
+    """Run a small battery of the pins above; return False if any fails."""
+    try:
+        test_scores_handworked_example()
+        for s in range(2):
+            test_scores_equal_exact_rational_brute_force(s)
+        for s in range(2):
+            test_topk_equals_counting_definition(s, 3)
+        test_attention_handworked_example()
+        test_full_selection_equals_dense_causal_sdpa(96, 64)
+        test_decode_equals_prefill_last_row()
+    except AssertionError:
+        return False
+    return True
+
+
+def _wrong_topk_high_index(scores, k):
+    n = scores.shape[0]
+    order = np.lexsort((-np.arange(n), -scores))
+    m = min(k, n)
+    out = np.full(k, -1, dtype=np.int32)
+    out[:m] = np.sort(order[:m])
+    return out
+
+
+def _wrong_scores_no_relu(q_i, w, k_i):
+    return (k_i @ q_i.T) @ w + 0.0
+
+
+def _wrong_scores_no_weight(q_i, w, k_i):
+    return np.maximum(k_i @ q_i.T, 0).sum(1) + 0.0
+
+
+def _wrong_mqa_v_from_tail(q, kv_sel, d_v, scale):
+    if kv_sel.shape[0] == 0:
+        return np.zeros((q.shape[0], d_v)), np.full(q.shape[0], -np.inf)
+    z = scale * (q @ kv_sel.T)
+    p = np.exp(z - z.max(1, keepdims=True))
+    den = p.sum(1, keepdims=True)
+    return (p @ kv_sel[:, -d_v:]) / den, (z.max(1, keepdims=True) + np.log(den))[:, 0]
+
+
+def _wrong_valid_off_by_one(idx_row, t):
+    return idx_row[(idx_row >= 0) & (idx_row < t)]
+
+
+@pytest.mark.parametrize("name,attr,bad", [
+    ("tie-break to highest index", "topk_select", _wrong_topk_high_index),
+    ("ReLU dropped", "indexer_scores", _wrong_scores_no_relu),
+    ("head weights dropped", "indexer_scores", _wrong_scores_no_weight),
+    ("V taken from the wrong end of the row", "sparse_mqa", _wrong_mqa_v_from_tail),
+    ("causal bound off by one", "valid_selected", _wrong_valid_off_by_one),
+])
+def test_planted_mistakes_are_caught(monkeypatch, name, attr, bad):
+    assert _pins_pass(False)
+    monkeypatch.setattr(orc, attr, bad)
+    assert not _pins_pass(True), f"planted mistake not caught: {name}"
