@@ -171,7 +171,7 @@ def valid_selected(idx_row: np.ndarray, t: int) -> np.ndarray:
 
 def prefill_indexer_topk(inp: dict, rows=None) -> np.ndarray:
     """Top-k index rows for the given query rows (local row numbers; default all)."""
-    q_i = decode_e4m3fn(inp["q_idx"])
+    q_codes = _np(inp["q_idx"])               # FP8 bytes; rows decoded one at a time
     k_i = decode_e4m3fn(inp["k_idx"])
     w = _np(inp["w"]).astype(np.float64)
     q_pos = _np(inp["q_pos"]).astype(np.int64)
@@ -180,7 +180,10 @@ def prefill_indexer_topk(inp: dict, rows=None) -> np.ndarray:
     out = np.empty((len(rows), k), dtype=np.int32)
     for r, i in enumerate(rows):
         t = int(q_pos[i])
-        sc = indexer_scores(q_i[i], w[i], k_i[: t + 1])
+        if t < 0:
+            out[r] = -1
+            continue
+        sc = indexer_scores(decode_e4m3fn(q_codes[i]), w[i], k_i[: t + 1])
         out[r] = topk_select(sc, k)
     return out
 
@@ -210,8 +213,8 @@ def prefill(inp: dict, rows=None, idx=None):
     return idx, o, lse
 
 
-def paged_rows(cache, page_table_row, n: int, page_size: int) -> np.ndarray:
-    """Logical rows 0..n-1 of one sequence from a paged cache (host copy; bf16 as uint16 bits).
+def paged_gather(cache, page_table_row, positions, page_size: int) -> np.ndarray:
+    """Logical rows ``positions`` of one sequence from a paged cache (host copy; bf16 as bits).
 
     Row s lives at page page_table_row[s // page_size], slot s % page_size.  Paging with
     page size 64 is the serving layout named on the mundobytes.com page (section "Quick guide
@@ -219,17 +222,22 @@ def paged_rows(cache, page_table_row, n: int, page_size: int) -> np.ndarray:
     kernels and ecosystem support").
     """
     pt = _np(page_table_row).astype(np.int64)
-    s = np.arange(n)
+    s = np.asarray(positions, dtype=np.int64)
     pages, slots = pt[s // page_size], s % page_size
     try:
         import torch
-        if isinstance(cache, torch.Tensor):     # gather on the tensor's device, copy n rows
+        if isinstance(cache, torch.Tensor):     # gather on the tensor's device, copy the rows
             dev = cache.device
             rows = cache[torch.as_tensor(pages, device=dev), torch.as_tensor(slots, device=dev)]
             return _np(rows)
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(cache)[pages, slots]
+
+
+def paged_rows(cache, page_table_row, n: int, page_size: int) -> np.ndarray:
+    """Logical rows 0..n-1 of one sequence from a paged cache."""
+    return paged_gather(cache, page_table_row, np.arange(n), page_size)
 
 
 def decode(inp: dict, seqs=None, idx=None):
@@ -262,9 +270,10 @@ def decode(inp: dict, seqs=None, idx=None):
         else:
             out_idx[r] = np.asarray(idx[r])
         sel = valid_selected(out_idx[r], t)
-        kv_bits = paged_rows(kvc, pt[b], n, P)
+        kv_sel = decode_bf16(paged_gather(kvc, pt[b], sel, P)) if len(sel) else \
+            np.zeros((0, kvc.shape[-1]))
         q = decode_bf16(inp["q"][b])
-        o[r], lse[r] = sparse_mqa(q, decode_bf16(kv_bits[sel]), d_v, scale)
+        o[r], lse[r] = sparse_mqa(q, kv_sel, d_v, scale)
     return out_idx, o, lse
 
 
@@ -290,6 +299,6 @@ def selected_pairs(L: int, k: int) -> int:
 
 __all__ = [
     "E4M3FN", "decode_e4m3fn", "decode_bf16", "indexer_scores", "topk_select", "sparse_mqa",
-    "valid_selected", "prefill_indexer_topk", "prefill", "paged_rows", "decode", "row_work",
+    "valid_selected", "prefill_indexer_topk", "prefill", "paged_gather", "paged_rows", "decode", "row_work",
     "causal_pairs", "selected_pairs",
 ]
