@@ -143,3 +143,145 @@ __device__ int block_stable_keep(Load load, int n, u32 T, int r, Emit emit, Sele
 }
 
 }  // namespace dsa
+
+namespace dsa {
+
+// ------------------------------------------------------------------------------------------
+// Wave-level versions (one wave selects over one list; no block barriers).  `hist` is this
+// wave's private 256-bin LDS histogram.  Lists live in global memory, so every pass loads
+// U items per lane before using any of them, keeping U loads in flight.
+// ------------------------------------------------------------------------------------------
+constexpr int kSelU = 16;
+
+template <class KeyOf>
+__device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_out, int& r_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  // bits on which all keys agree need no pass
+  u32 kand = 0xffffffffu, kor = 0u;
+  for (int base = 0; base < n; base += kWave * kSelU) {
+    u32 kk[kSelU];
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const int i = base + u * kWave + lane;
+      kk[u] = i < n ? key_of(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const bool in = base + u * kWave + lane < n;
+      kand &= in ? kk[u] : 0xffffffffu;
+      kor |= in ? kk[u] : 0u;
+    }
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    kand &= (u32)__shfl_xor((int)kand, o);
+    kor |= (u32)__shfl_xor((int)kor, o);
+  }
+  const u32 diff = kand ^ kor;
+  u32 prefix = kand & ~diff, pmask = ~diff;  // common bits are fixed from the start
+  int remaining = k;
+  if (diff != 0u) {
+    const int top = 31 - __builtin_clz(diff);
+#pragma unroll 1
+    for (int hi = top; hi >= 0; hi -= 8) {
+      const int shift = hi >= 7 ? hi - 7 : 0;
+      const u32 dmask = (hi >= 7) ? 255u : ((1u << (hi + 1)) - 1u);
+      if ((diff & (dmask << shift)) == 0u) continue;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      for (int base = 0; base < n; base += kWave * kSelU) {
+        u32 kk[kSelU];
+#pragma unroll
+        for (int u = 0; u < kSelU; ++u) {
+          const int i = base + u * kWave + lane;
+          kk[u] = i < n ? key_of(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kSelU; ++u) {
+          const bool match = (base + u * kWave + lane < n) && (kk[u] & pmask) == prefix;
+          const u32 d = (kk[u] >> shift) & dmask;
+          const uint64_t mm = wave_ballot(match);
+          if (mm == 0ull) continue;
+          // all matching lanes on one digit (the common case): one atomic for the wave
+          const int first = __builtin_ctzll(mm);
+          const u32 d0 = __builtin_amdgcn_readlane(d, first);
+          const uint64_t same = wave_ballot(match && d == d0);
+          if (same == mm) {
+            if (lane == first) atomicAdd(&hist[d0], (u32)__builtin_popcountll(mm));
+          } else if (match) {
+            atomicAdd(&hist[d], 1u);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      u32 c[4];
+      int tot = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        c[b] = hist[4 * lane + b];
+        tot += (int)c[b];
+      }
+      int incl = tot;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_down(incl, o);
+        if (lane + o < kWave) incl += t;
+      }
+      const int excl = incl - tot;
+      int dsel = 0, above = 0;
+      const bool mine = (excl < remaining && remaining <= incl);
+      if (mine) {
+        int cum = excl;
+        for (int b = 3; b >= 0; --b) {
+          if (cum + (int)c[b] >= remaining) {
+            dsel = 4 * lane + b;
+            above = cum;
+            break;
+          }
+          cum += (int)c[b];
+        }
+      }
+      const uint64_t who = wave_ballot(mine);
+      const int src = __builtin_ctzll(who | (1ull << 63));
+      dsel = __builtin_amdgcn_readlane(dsel, src);
+      above = __builtin_amdgcn_readlane(above, src);
+      remaining -= above;
+      prefix = (prefix & ~(dmask << shift)) | ((u32)dsel << shift);
+      pmask |= dmask << shift;
+    }
+  }
+  T_out = prefix;
+  r_out = remaining;
+}
+
+// Wave-level stable keep (see block_stable_keep).  All U chunks of a batch are loaded before
+// any item of the batch is emitted, and emits go below the batch end, so in-place use is safe.
+template <class Load, class Emit>
+__device__ int wave_stable_keep(Load load, int n, u32 T, int r, Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int ties = 0, out = 0;
+  for (int base = 0; base < n; base += kWave * kSelU) {
+    decltype(load(0)) item[kSelU];
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const int i = base + u * kWave + lane;
+      item[u] = load(i < n ? i : 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const bool in = base + u * kWave + lane < n;
+      const bool gt = in && item[u].key > T;
+      const bool eq = in && item[u].key == T;
+      const uint64_t beq = wave_ballot(eq);
+      const int rank = ties + lanes_below(beq);
+      const bool keep = gt || (eq && rank < r);
+      const uint64_t bk = wave_ballot(keep);
+      if (keep) emit(item[u], out + lanes_below(bk));
+      ties += __builtin_popcountll(beq);
+      out += __builtin_popcountll(bk);
+    }
+  }
+  return out;
+}
+
+}  // namespace dsa

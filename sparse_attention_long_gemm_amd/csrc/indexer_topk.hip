@@ -33,12 +33,14 @@ namespace dsa {
 
 namespace {
 
-constexpr int QB = 16;       // query rows per workgroup
-constexpr int NWAVE = 4;     // waves per workgroup, 16 indexer heads each
+constexpr int QB = 16;         // query rows per workgroup
+constexpr int NWAVE = 8;       // 4 head groups x 2 key-tile parities
 constexpr int NT = NWAVE * kWave;
-constexpr int BK = 64;       // keys per tile
-constexpr int HPW = 16;      // indexer heads per wave
-constexpr int PSTR = BK + 4; // padded LDS row stride (floats) of the per-wave partial scores
+constexpr int BK = 64;         // keys per tile; one iteration covers 2 tiles = 128 keys
+constexpr int BK2 = 2 * BK;
+constexpr int HPW = 16;        // indexer heads per wave
+constexpr int PSTR = BK + 4;   // padded LDS row stride (floats) of the partial scores
+constexpr int RPW = QB / NWAVE;  // query rows owned by each wave (filter + selection)
 
 __device__ __forceinline__ v4i load16(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
 
@@ -68,20 +70,18 @@ struct CandItem {
 };
 
 struct PrefillShared {
-  float part[NWAVE][QB][PSTR];
-  float thr[QB];
-  int cnt[QB];
-  int need;
-  SelectShared sel;
+  float part[2][2][4][QB][PSTR];  // [buffer][tile parity][head group][row][key]
+  u32 hist[NWAVE][256];           // per-wave radix histograms
+  int full[2][NWAVE];             // [iteration parity][wave]: a row of the wave is near full
 };
 
-// Cut row q's candidate list (n > top_k items, position order) to its exact top_k, in place;
-// returns the new threshold (the top_k-th score).
-__device__ float compact_row(float* cs, int32_t* ci, int n, int top_k, SelectShared& sel) {
+// Cut a row's candidate list (n > top_k items in position order) to its exact top_k in
+// place, using one wave; returns the top_k-th score, the row's new threshold.
+__device__ float wave_compact(float* cs, int32_t* ci, int n, int top_k, u32* hist) {
   u32 T;
   int r;
-  block_radix_select<NT>([&](int i) { return ord_key(cs[i]); }, n, top_k, sel, T, r);
-  block_stable_keep<NT>(
+  wave_radix_select([&](int i) { return ord_key(cs[i]); }, n, top_k, hist, T, r);
+  wave_stable_keep(
       [&](int i) { CandItem it; it.score = cs[i]; it.pos = ci[i]; it.key = ord_key(it.score); return it; },
       n, T, r,
       [&](const CandItem& it, int p) {
@@ -89,8 +89,7 @@ __device__ float compact_row(float* cs, int32_t* ci, int n, int top_k, SelectSha
           cs[p] = it.score;
           ci[p] = it.pos;
         }
-      },
-      sel);
+      });
   return key_to_float(T);
 }
 
@@ -102,17 +101,15 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   __shared__ PrefillShared sh;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
+  const int hg = wave & 3;       // head group: heads 16hg..16hg+15
+  const int kh = wave >> 2;      // key-tile parity: tile 2i+kh of iteration i
   const int lane = tid & (kWave - 1);
-  const int g = lane >> 4;     // lane group: bytes [32g, 32g+32) of a row; output rows 4g..4g+3
-  const int c16 = lane & 15;   // output column = query row within the block
+  const int g = lane >> 4;       // lane group: bytes [32g, 32g+32) of a row; output rows 4g..4g+3
+  const int c16 = lane & 15;     // output column = query row within the block
   const int q0 = blockIdx.x * QB;
+  const bool heads_here = HPW * hg < H_I;
 
-  // ---- per-row state ----
-  if (tid < QB) {
-    sh.thr[tid] = -__builtin_inff();
-    sh.cnt[tid] = 0;
-  }
-  // last candidate position of each row of the block, and of the block
+  // ---- last candidate position of each row (t clamped to the keys; -1: nothing) ----
   int t_lane = -1;
   {
     const int q = q0 + c16;
@@ -120,6 +117,15 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   }
   int t_max = t_lane;
   for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
+  // rows owned by this wave, their state (wave-uniform)
+  int t_own[RPW], cnt[RPW];
+  float thr[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    t_own[rr] = __shfl(t_lane, RPW * wave + rr);
+    cnt[rr] = 0;
+    thr[rr] = -__builtin_inff();
+  }
 
   // ---- queries of this wave's 16 heads for the 16 rows (MFMA B operand) ----
   v8i qf[HPW];
@@ -128,103 +134,124 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     const int q = q0 + c16;
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const int h = wave * HPW + j;
+      const int h = hg * HPW + j;
       const bool ok = (q < n_q) && (h < H_I);
       qf[j] = load_row32(q_idx + ((size_t)q * H_I + h) * d_I, g, d_I, ok);
       wv[j] = ok ? w[(size_t)q * H_I + h] : 0.f;
     }
   }
-  __syncthreads();
 
-  const int n_tiles = (t_max + BK) / BK;  // tiles covering keys 0..t_max
-#pragma unroll 1
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int s0 = tile * BK;
-    // ---- partial scores of this wave's heads: keys s0..s0+63 x 16 rows ----
+  const int n_iter = (t_max + BK2) / BK2;  // iterations covering keys 0..t_max
+  v8i a_cur[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int s = s0 + 16 * f + c16;
-      const v8i a = load_row32(k_idx + (size_t)s * d_I, g, d_I, s < n_keys);
-      float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-#pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        const v4f x = mfma_fp8(a, qf[j]);
-        acc0 = fmaf(wv[j], fmaxf(x[0], 0.f), acc0);
-        acc1 = fmaf(wv[j], fmaxf(x[1], 0.f), acc1);
-        acc2 = fmaf(wv[j], fmaxf(x[2], 0.f), acc2);
-        acc3 = fmaf(wv[j], fmaxf(x[3], 0.f), acc3);
-      }
-      // lane holds keys 16f + 4g + (0..3) of query row c16
-      float* dst = &sh.part[wave][c16][16 * f + 4 * g];
-      *reinterpret_cast<v4f*>(dst) = v4f{acc0, acc1, acc2, acc3};
-    }
-    __syncthreads();
-    // ---- head sum, causal mask, threshold filter, ordered append (wave owns 4 rows) ----
-#pragma unroll 1
-    for (int rr = 0; rr < QB / NWAVE; ++rr) {
-      const int r = wave * (QB / NWAVE) + rr;
-      const int q = q0 + r;
-      if (q >= n_q) break;
-      const int t = min(q_pos[q], n_keys - 1);
-      if (s0 > t) continue;
-      const int s = s0 + lane;
-      const float sc = ((sh.part[0][r][lane] + sh.part[1][r][lane]) + sh.part[2][r][lane]) +
-                       sh.part[3][r][lane];
-      const bool pass = (s <= t) && (sc > sh.thr[r]);
-      const uint64_t m = wave_ballot(pass);
-      const int c = sh.cnt[r];
-      if (pass) {
-        const int p = c + lanes_below(m);
-        cand_score[(size_t)q * cap + p] = (sc == 0.f) ? 0.f : sc;
-        cand_pos[(size_t)q * cap + p] = s;
-      }
-      if (lane == 0) sh.cnt[r] = c + __builtin_popcountll(m);
-    }
-    __syncthreads();
-    // ---- cut any list that could overflow on the next tile ----
-    if (tile + 1 < n_tiles) {
-      bool any = false;
-#pragma unroll 1
-      for (int r = 0; r < QB; ++r) any |= (sh.cnt[r] + BK > cap);
-      if (any) {
-#pragma unroll 1
-        for (int r = 0; r < QB; ++r) {
-          const int n = sh.cnt[r];
-          if (n + BK <= cap) continue;
-          const int q = q0 + r;
-          const float T = compact_row(cand_score + (size_t)q * cap, cand_pos + (size_t)q * cap,
-                                      n, top_k, sh.sel);
-          __syncthreads();
-          if (tid == 0) {
-            sh.thr[r] = T;
-            sh.cnt[r] = top_k;
-          }
-          __syncthreads();
-        }
-      }
-    }
+  for (int f = 0; f < 4; ++f) {
+    const int s = kh * BK + 16 * f + c16;
+    a_cur[f] = load_row32(k_idx + (size_t)s * d_I, g, d_I, heads_here && s < n_keys);
   }
 
-  // ---- final exact selection of every row ----
 #pragma unroll 1
-  for (int r = 0; r < QB; ++r) {
-    const int q = q0 + r;
-    if (q >= n_q) break;
-    const int n = sh.cnt[r];
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    // ---- prefetch the next iteration's key fragments ----
+    v8i a_nxt[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int s = (it + 1) * BK2 + kh * BK + 16 * f + c16;
+      a_nxt[f] = load_row32(k_idx + (size_t)s * d_I, g, d_I,
+                            heads_here && it + 1 < n_iter && s < n_keys);
+    }
+    // ---- partial scores of this wave's 16 heads: its 64 keys x 16 rows ----
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+      if (heads_here) {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          const v4f x = mfma_fp8(a_cur[f], qf[j]);
+          acc0 = fmaf(wv[j], fmaxf(x[0], 0.f), acc0);
+          acc1 = fmaf(wv[j], fmaxf(x[1], 0.f), acc1);
+          acc2 = fmaf(wv[j], fmaxf(x[2], 0.f), acc2);
+          acc3 = fmaf(wv[j], fmaxf(x[3], 0.f), acc3);
+        }
+      }
+      // lane holds keys 16f + 4g + (0..3) of query row c16
+      *reinterpret_cast<v4f*>(&sh.part[buf][kh][hg][c16][16 * f + 4 * g]) =
+          v4f{acc0, acc1, acc2, acc3};
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) a_cur[f] = a_nxt[f];
+    __syncthreads();
+
+    // ---- cut candidate lists, all waves together (a cut stalls the whole workgroup at the
+    // next barrier, so cuts are batched): when any row of the workgroup ended the previous
+    // iteration with less than one iteration of room, every row past half of its slack is cut
+    bool any_full = false;
+    if (it > 0) {
+#pragma unroll
+      for (int v = 0; v < NWAVE; ++v) any_full |= sh.full[(it - 1) & 1][v] != 0;
+    }
+    if (any_full) {
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const int q = q0 + RPW * wave + rr;
+        if (q >= n_q || it * BK2 > t_own[rr] || 2 * cnt[rr] <= top_k + cap) continue;
+        thr[rr] = wave_compact(cand_score + (size_t)q * cap, cand_pos + (size_t)q * cap,
+                               cnt[rr], top_k, sh.hist[wave]);
+        cnt[rr] = top_k;
+      }
+    }
+
+    // ---- this wave's rows: head sum, causal mask, threshold filter, ordered append ----
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int r = RPW * wave + rr;
+      const int q = q0 + r;
+      const int t = t_own[rr];
+      if (q >= n_q || it * BK2 > t) continue;
+      float* cs = cand_score + (size_t)q * cap;
+      int32_t* ci = cand_pos + (size_t)q * cap;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int s = it * BK2 + half * BK + lane;
+        const float sc = ((sh.part[buf][half][0][r][lane] + sh.part[buf][half][1][r][lane]) +
+                          sh.part[buf][half][2][r][lane]) + sh.part[buf][half][3][r][lane];
+        const bool pass = (s <= t) && (sc > thr[rr]);
+        const uint64_t m = wave_ballot(pass);
+        if (pass) {
+          const int p = cnt[rr] + lanes_below(m);
+          cs[p] = (sc == 0.f) ? 0.f : sc;
+          ci[p] = s;
+        }
+        cnt[rr] += __builtin_popcountll(m);
+      }
+    }
+    // flag rows that could overflow on the next iteration; they are cut after its barrier
+    bool full = false;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr)
+      full |= (q0 + RPW * wave + rr < n_q) && cnt[rr] + BK2 > cap && (it + 1) * BK2 <= t_own[rr];
+    if (lane == 0) sh.full[it & 1][wave] = full ? 1 : 0;
+  }
+
+  // ---- final exact selection of this wave's rows ----
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int q = q0 + RPW * wave + rr;
+    if (q >= n_q) continue;
+    const int n = cnt[rr];
     int32_t* orow = out_idx + (size_t)q * top_k;
     const float* cs = cand_score + (size_t)q * cap;
     const int32_t* ci = cand_pos + (size_t)q * cap;
     if (n <= top_k) {
-      for (int i = tid; i < top_k; i += NT) orow[i] = (i < n) ? ci[i] : -1;
+      for (int i = lane; i < top_k; i += kWave) orow[i] = (i < n) ? ci[i] : -1;
     } else {
       u32 T;
-      int rr;
-      block_radix_select<NT>([&](int i) { return ord_key(cs[i]); }, n, top_k, sh.sel, T, rr);
-      block_stable_keep<NT>(
+      int r;
+      wave_radix_select([&](int i) { return ord_key(cs[i]); }, n, top_k, sh.hist[wave], T, r);
+      wave_stable_keep(
           [&](int i) { CandItem it; it.score = cs[i]; it.pos = ci[i]; it.key = ord_key(it.score); return it; },
-          n, T, rr, [&](const CandItem& it, int p) { if (p < top_k) orow[p] = it.pos; }, sh.sel);
+          n, T, r, [&](const CandItem& it, int p) { if (p < top_k) orow[p] = it.pos; });
     }
-    __syncthreads();
   }
 }
 
@@ -322,9 +349,10 @@ __global__ __launch_bounds__(TOPK_NT) void topk_rows_kernel(const float* __restr
 // Host launchers
 // ------------------------------------------------------------------------------------------
 int indexer_cap(int top_k) {
-  int cap = 2 * top_k;
-  if (cap < top_k + BK) cap = top_k + BK;
-  return (cap + BK - 1) / BK * BK;
+  // room for top_k kept items plus at least two iterations of appends
+  int cap = 2 * top_k + BK2;
+  if (cap < top_k + 2 * BK2) cap = top_k + 2 * BK2;
+  return (cap + BK2 - 1) / BK2 * BK2;
 }
 
 size_t indexer_prefill_ws(int n_q, int top_k) {

@@ -285,32 +285,38 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   }
 }
 
-// Merge n_split partial results of each (query, head): weights exp2(m_i - M).
+// Merge the n_split partial results of one (query, head): weights exp2(m_i - M).
+// One workgroup per (query, head); each thread owns 4 consecutive dims.
 template <int DV>
-__global__ __launch_bounds__(256) void mqa_combine_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_ml,
-                                                          int H, int n_split,
-                                                          uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse) {
-  const int qi = blockIdx.x;
-  for (int hd = threadIdx.x; hd < H * DV; hd += 256) {
-    const int h = hd / DV, d = hd - h * DV;
-    float M = -__builtin_inff();
-    for (int i = 0; i < n_split; ++i)
-      M = fmaxf(M, part_ml[(((size_t)qi * n_split + i) * H + h) * 2]);
-    float L = 0.f, acc = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int i = 0; i < n_split; ++i) {
-        const size_t b = ((size_t)qi * n_split + i) * H + h;
-        const float wgt = exp2f(part_ml[b * 2] - M);
-        L += wgt * part_ml[b * 2 + 1];
-        acc += wgt * part_o[b * DV + d];
-      }
+__global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml,
+                                                             int H, int n_split,
+                                                             uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse) {
+  const int qi = blockIdx.x / H;
+  const int h = blockIdx.x - qi * H;
+  const size_t base = (size_t)qi * n_split * H + h;   // partial i lives at base + i*H
+  float M = -__builtin_inff();
+  for (int i = 0; i < n_split; ++i) M = fmaxf(M, part_ml[(base + (size_t)i * H) * 2]);
+  float L = 0.f;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  const int d = 4 * threadIdx.x;
+  if (M != -__builtin_inff()) {
+    for (int i = 0; i < n_split; ++i) {
+      const size_t b = base + (size_t)i * H;
+      const float wgt = exp2f(part_ml[b * 2] - M);
+      L += wgt * part_ml[b * 2 + 1];
+      const v4f v = *reinterpret_cast<const v4f*>(part_o + b * DV + d);
+      acc += wgt * v;
     }
-    out[((size_t)qi * H + h) * DV + d] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
-    if (lse != nullptr && d == 0)
-      lse[(size_t)qi * H + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -__builtin_inff();
   }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint2 o;
+  o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<uint2*>(out + ((size_t)qi * H + h) * DV + d) = o;
+  if (lse != nullptr && threadIdx.x == 0)
+    lse[(size_t)qi * H + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 template <int DK, int DV>
@@ -329,8 +335,8 @@ hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
                      a.lse, a.part_o, a.part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL((mqa_combine_kernel<DV>), dim3(a.n_q), dim3(256), 0, stream, a.part_o,
-                     a.part_ml, a.H, a.n_split, a.out, a.lse);
+  hipLaunchKernelGGL((mqa_combine_kernel<DV>), dim3(a.n_q * a.H), dim3(DV / 4), 0, stream,
+                     a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
   return hipGetLastError();
 }
 
