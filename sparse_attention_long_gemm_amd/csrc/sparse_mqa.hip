@@ -10,15 +10,18 @@
 // (hg, dh) owns heads 32hg..32hg+31 and half dh of the dimensions: its share of the queries
 // (dims [D_k/2 * dh, +D_k/2)) stays in registers as the B operand of
 // v_mfma_f32_32x32x16_bf16 and its fp32 output accumulators (dims [D_v/2 * dh, +D_v/2)) stay in
-// registers for the whole slice.  Per chunk of 32 selected rows the workgroup gathers the rows
-// (coalesced 16-byte pieces) into LDS twice: row-major (A operand of S^T = K Q^T, keys x
-// heads) and transposed V^T (A operand of O^T += V^T P^T, dims x heads).  The two waves of a
-// head group add their half-dimension partial logits through LDS (in a fixed order, so both
-// hold the same sums).  With keys on the MFMA rows, each lane owns one head, so the
-// online-softmax row max and sum stay in the lane (plus one exchange with the partner lane
-// that holds the other 16 keys), and the probabilities already sit in the B-operand layout of
-// the value product once packed to bf16; V^T's key order inside each 16-key group is
-// permuted to match that layout.
+// registers for the whole slice.  The selected rows are gathered 32 at a time straight from
+// global memory into a double-buffered LDS tile (global_load_lds, 16 bytes per lane, the next
+// chunk in flight while the current one is computed).  The tile is row-major with one 16-byte
+// pad per row (row stride 2 D_k + 16 bytes spreads both read patterns over all LDS banks and
+// keeps every address base + constant), so it is the A operand of S^T = K Q^T as is; the A
+// operand of O^T += V^T P^T is read from the same tile with the transposing LDS read
+// (ds_read_b64_tr_b16), so no transposed copy is stored.  The two waves of a head group add
+// their half-dimension partial logits through LDS (in a fixed order, so both hold the same
+// sums).  With keys on the MFMA rows, each lane owns one head, so the online-softmax row max
+// and sum stay in the lane (plus one exchange with the partner lane that holds the other 16
+// keys), and the probabilities already sit in the B-operand layout of the value product once
+// packed to bf16.
 //
 // Decode (paged) splits each sequence's selected rows over n_split workgroups; partial
 // (unnormalised o, running max, running sum) triples are merged by mqa_combine_kernel.
@@ -33,10 +36,19 @@ constexpr int NW = 8;            // 4 head groups x 2 dimension halves
 constexpr int NT = NW * kWave;
 constexpr int HPW = 32;          // heads per wave
 constexpr int CH = 32;           // selected rows per chunk
-constexpr int VSTR = CH * 2 + 16; // V^T row stride in bytes (padded against bank conflicts)
 constexpr int MAX_ROWS = 2048;   // selected rows per workgroup (top_k <= 2048)
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
 __device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// Workgroup barrier that orders LDS traffic only: it does not wait for outstanding global
+// loads, so the asynchronous gather of the next chunk stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -48,21 +60,54 @@ __device__ __forceinline__ v8bf as_v8bf(const v4i& x) {
   return r;
 }
 
-// Position of chunk-relative key r inside V^T: within each 16-key group, half h of the lanes
-// reads positions 8h..8h+7, which must hold keys {4h..4h+3, 8+4h..8+4h+3} (the keys whose
-// probabilities those lanes hold after the S^T product).
-__device__ __forceinline__ int vt_pos_of_quad(int kq) {
-  return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq & 3) >> 1);
-}
-
-template <int DK, int DV>
-struct MqaShared {
-  static constexpr int KSTR = DK * 2 + 16;  // padded row stride (bytes) of the row-major tile
-  alignas(16) uint8_t ks[CH * KSTR];
-  alignas(16) uint8_t vt[DV * VSTR];
-  alignas(16) float sx[NW][16][kWave];      // half-dimension partial logits of each wave
-  int rows[MAX_ROWS];                       // physical row of each selected entry, or -1
+template <int DK>
+struct Tile {
+  static constexpr int NCH = DK / 8;                   // 16-byte chunks of a row
+  static constexpr int SLOTS = NCH + 1;                // + one pad slot
+  static constexpr int RS = 16 * SLOTS;                // row stride (bytes)
+  static constexpr int LOADS = (CH * SLOTS + kWave - 1) / kWave;  // wave-loads per chunk
+  static constexpr int BYTES = LOADS * kWave * 16;
 };
+
+// Query fragments of the last QL k-steps of each wave live in LDS instead of registers (this
+// keeps the 576-wide instance within 256 VGPRs per wave at 2 waves per SIMD).
+template <int DK>
+struct QSplit {
+  static constexpr int NKS = DK / 32;
+  static constexpr int QL = NKS >= 16 ? 4 : 0;
+  static constexpr int QR = NKS - QL;
+};
+
+// (The two row-tile buffers are separate __shared__ objects: reads of one buffer then provably
+// do not alias the asynchronous fill of the other, so no wait for that fill is inserted.)
+template <int DK>
+struct MqaShared {
+  alignas(16) float sx[NW][16][kWave];       // half-dimension partial logits of each wave
+  alignas(16) v8bf qs[NW][QSplit<DK>::QL > 0 ? QSplit<DK>::QL : 1][kWave];  // LDS query part
+  int rows[MAX_ROWS];                        // physical row of each selected entry, or -1
+};
+
+// Issue the gather of chunk c (32 rows) into `tile`: wave-load j covers 64 consecutive 16-byte
+// tile slots; lane i fills slot 64j + i (pad slots and slots past the tile get a harmless load
+// of the first chunk of the KV array).
+template <int DK>
+__device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __restrict__ kv,
+                                             const int* rows, int c, int nrows, int wave,
+                                             int lane) {
+  using T = Tile<DK>;
+  for (int j = wave; j < T::LOADS; j += NW) {
+    const int u = j * kWave + lane;
+    const int r = u / T::SLOTS;
+    const int p = u - r * T::SLOTS;
+    const int e = c * CH + r;
+    int row = (r < CH && e < nrows) ? rows[e] : -1;
+    const bool real = row >= 0 && p < T::NCH;
+    const uint16_t* src = real ? kv + (size_t)row * DK + 8 * p : kv;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(tile + 16 * kWave * j),
+                                     16, 0, 0);
+  }
+}
 
 template <int DK, int DV, bool PAGED>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
@@ -73,12 +118,13 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   static_assert(DK % 32 == 0 && DV % 64 == 0 && DV <= DK, "shape");
-  using Sh = MqaShared<DK, DV>;
-  constexpr int KSTR = Sh::KSTR;
-  constexpr int NP = DK / 8;       // 16-byte pieces per row
-  constexpr int NKS = DK / 32;     // k-steps of this wave's half of the S^T product
-  constexpr int NDB = DV / 64;     // 32-dim blocks of this wave's half of the output
+  using Sh = MqaShared<DK>;
+  constexpr int NKS = DK / 32;           // k-steps of this wave's half of the S^T product
+  constexpr int NDB = DV / 64;           // 32-dim blocks of this wave's half of the output
+  constexpr int RS = Tile<DK>::RS;
   __shared__ Sh sh;
+  __shared__ __attribute__((aligned(16))) uint8_t kt0[Tile<DK>::BYTES];  // selected rows, buffer 0
+  __shared__ __attribute__((aligned(16))) uint8_t kt1[Tile<DK>::BYTES];  // selected rows, buffer 1
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -90,9 +136,9 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   const int qi = blockIdx.x;
   const int sp = blockIdx.y;
   const int head = hg * HPW + c32;
+  const bool head_ok = head < H;
   const int kd0 = dh * (DK / 2);    // first key dim of this wave's logit half
   const int vd0 = dh * (DV / 2);    // first value dim of this wave's output half
-  const bool head_ok = head < H;
 
   // last attendable position
   int t;
@@ -125,14 +171,19 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   }
 
   // ---- queries of this wave's heads: B operand, k-step ks holds dims kd0 + 16ks + 8hf .. +8
-  v8bf qf[NKS];
+  // (k-steps >= QR are kept in LDS)
+  constexpr int QR = QSplit<DK>::QR;
+  v8bf qf[QR];
   {
     const uint16_t* qrow = q + ((size_t)qi * H + (head_ok ? head : 0)) * DK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       v4i x = {0, 0, 0, 0};
       if (head_ok) x = ld16(qrow + kd0 + 16 * ks + 8 * hf);
-      qf[ks] = as_v8bf(x);
+      if (ks < QR)
+        qf[ks < QR ? ks : 0] = as_v8bf(x);
+      else
+        sh.qs[wave][ks - QR][lane] = as_v8bf(x);
     }
   }
 
@@ -143,116 +194,109 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
   float m_run = -__builtin_inff();
   float l_run = 0.f;
-  __syncthreads();
 
   const int n_chunks = (nrows + CH - 1) / CH;
-#pragma unroll 1
-  for (int c = 0; c < n_chunks; ++c) {
-    // ---- gather 32 selected rows: row-major tile + permuted V^T ----
-#pragma unroll 1
-    for (int task = tid; task < 8 * NP; task += NT) {
-      const int kq = task / NP;
-      const int p = task - kq * NP;
-      v4i rv[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int e = c * CH + 4 * kq + rr;
-        const int row = (e < nrows) ? sh.rows[e] : -1;
-        rv[rr] = v4i{0, 0, 0, 0};
-        if (row >= 0) rv[rr] = ld16(kv + (size_t)row * DK + 8 * p);
-        *reinterpret_cast<v4i*>(&sh.ks[(4 * kq + rr) * KSTR + 16 * p]) = rv[rr];
-      }
-      if (8 * p < DV) {
-        const int pos0 = vt_pos_of_quad(kq);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const u32 a0 = (u32)rv[0][m], a1 = (u32)rv[1][m], a2 = (u32)rv[2][m], a3 = (u32)rv[3][m];
-          // dim 8p + 2m (low halves) and 8p + 2m + 1 (high halves), 4 keys each
-          uint2 lo, hi;
-          lo.x = (a0 & 0xffffu) | (a1 << 16);
-          lo.y = (a2 & 0xffffu) | (a3 << 16);
-          hi.x = (a0 >> 16) | (a1 & 0xffff0000u);
-          hi.y = (a2 >> 16) | (a3 & 0xffff0000u);
-          *reinterpret_cast<uint2*>(&sh.vt[(8 * p + 2 * m) * VSTR + 2 * pos0]) = lo;
-          *reinterpret_cast<uint2*>(&sh.vt[(8 * p + 2 * m + 1) * VSTR + 2 * pos0]) = hi;
-        }
-      }
-    }
-    __syncthreads();
+  __syncthreads();   // rows[] complete
+  if (n_chunks > 0) gather_chunk<DK>(kt0, kv, sh.rows, 0, nrows, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // per-lane byte offsets inside a tile:
+  //  S^T A operand, k-step ks: row c32, dims kd0 + 16ks + 8hf .. +8  ->  qk_off + 32 ks
+  const int qk_off = c32 * RS + 2 * (kd0 + 8 * hf);
+  //  transposing read of the value product: input lane (m, q) of its 16-lane group points at
+  //  dims D + 4q of key 16k2 + 4hf + m (+8 for the second half of the k-slots), so output
+  //  lane j holds dim D + j; D = vd0 + 32d + 16 * (group parity)
+  const int tq = lane & 3, tm = (lane & 15) >> 2;
+  const int tr_off = (4 * hf + tm) * RS + 2 * (vd0 + 16 * ((lane >> 4) & 1) + 4 * tq);
+
+  auto step = [&](const lds_u8* tile, uint8_t* next_tile, int c) {
+    // ---- prefetch the next chunk into the other buffer ----
+    if (c + 1 < n_chunks) gather_chunk<DK>(next_tile, kv, sh.rows, c + 1, nrows, wave, lane);
 
     // ---- S^T = K Q^T for 32 keys x this wave's 32 heads, over its half of the dims ----
     v16f sp_;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sp_[i] = 0.f;
+    const lds_u8* qk_base = tile + qk_off;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const v8bf a = as_v8bf(ld16(&sh.ks[c32 * KSTR + 2 * (kd0 + 16 * ks + 8 * hf)]));
-      sp_ = mfma_bf16(a, qf[ks], sp_);
+      const v8bf b = ks < QR ? qf[ks < QR ? ks : 0] : sh.qs[wave][ks < QR ? 0 : ks - QR][lane];
+      const v4i av = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(qk_base + 32 * ks);
+      sp_ = mfma_bf16(as_v8bf(av), b, sp_);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sh.sx[wave][i][lane] = sp_[i];
-    __syncthreads();
-    float s[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = sh.sx[hg][i][lane] + sh.sx[hg + 4][i][lane];
+    lds_barrier();
 
-    // ---- online softmax (lane = head; element i is key 8(i/4) + 4hf + i%4) ----
-    float z[16];
+    // ---- online softmax (lane = head; element i is key 8(i/4) + 4hf + i%4), two passes over
+    // the logits in LDS so that only the packed probabilities stay in registers ----
+    // bit k of vmask: key k of the chunk is a valid selected row
+    const int ek = c * CH + c32;
+    const u32 vmask = (u32)wave_ballot(ek < nrows && sh.rows[ek < nrows ? ek : 0] >= 0);
+    // masked keys get a -inf bias (loads stay unconditional, no branches)
     float cmax = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
-      const int e = c * CH + key;
-      const bool ok = (e < nrows) && (sh.rows[e] >= 0);
-      z[i] = ok ? s[i] * scale_log2 : -__builtin_inff();
-      cmax = fmaxf(cmax, z[i]);
+      const float bias = ((vmask >> key) & 1u) ? 0.f : -__builtin_inff();
+      const float sv = sh.sx[hg][i][lane] + sh.sx[hg + 4][i][lane];
+      cmax = fmaxf(cmax, fmaf(sv, scale_log2, bias));
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
     const float m_new = fmaxf(m_run, cmax);
-    float alpha = 1.f;
+    const bool any = m_new != -__builtin_inff();
+    const float m_use = any ? m_new : 0.f;
+    const float alpha = any ? exp2f(m_run - m_new) : 1.f;
     float psum = 0.f;
-    float pr[16];
-    if (m_new == -__builtin_inff()) {
+    v8bf pb[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pr[i] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pr[i] = exp2f(z[i] - m_new);
-        psum += pr[i];
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+      const float bias = ((vmask >> key) & 1u) ? -m_use : -__builtin_inff();
+      const float sv = sh.sx[hg][i][lane] + sh.sx[hg + 4][i][lane];
+      const float pv = exp2f(fmaf(sv, scale_log2, bias));
+      psum += pv;
+      pb[i >> 3][i & 7] = (__bf16)pv;
     }
     m_run = m_new;
     l_run = l_run * alpha + psum;
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
+      for (int d = 0; d < NDB; ++d)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
 
-    v8bf pb[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pb[k2][j] = (__bf16)pr[8 * k2 + j];
-
-    // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T; V^T slots j of half hf hold key 16k2 + 8(j/4) + 4hf + j%4 ----
+    const lds_u8* tr_base = tile + tr_off;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const v8bf a =
-            as_v8bf(ld16(&sh.vt[(vd0 + 32 * d + c32) * VSTR + 2 * (16 * k2 + 8 * hf)]));
+        const lds_u8* pa = tr_base + 16 * k2 * RS + 64 * d;
+        const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa));
+        const v4s vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + 8 * RS));
+        v8bf a;
+        __builtin_memcpy(&a, &va, 8);
+        __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &vb, 8);
         o[d] = mfma_bf16(a, pb[k2], o[d]);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next chunk has landed
     __syncthreads();
+  };
+
+#pragma unroll 1
+  for (int c = 0; c < n_chunks; c += 2) {
+    step((const lds_u8*)kt0, kt1, c);
+    if (c + 1 < n_chunks) step((const lds_u8*)kt1, kt0, c + 1);
   }
 
   // ---- epilogue: lane holds head `head`, dims vd0 + 32d + 8(i/4) + 4hf + i%4 ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!head_ok) return;
   if (n_split == 1) {
-    if (!head_ok) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = out + ((size_t)qi * H + head) * DV;
 #pragma unroll
@@ -269,7 +313,6 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       lse[(size_t)qi * H + head] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
   } else {
-    if (!head_ok) return;
     float* po = part_o + (((size_t)qi * n_split + sp) * H + head) * DV;
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
