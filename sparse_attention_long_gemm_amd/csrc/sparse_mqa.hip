@@ -82,28 +82,47 @@ struct QSplit {
 // do not alias the asynchronous fill of the other, so no wait for that fill is inserted.)
 template <int DK>
 struct MqaShared {
-  alignas(16) float sx[NW][16][kWave];       // half-dimension partial logits of each wave
+  alignas(16) v4f sx[NW][4][kWave];          // half-dimension partial logits of each wave:
+                                             // [wave][i/4][lane] holds elements 4(i/4)..+3
   alignas(16) v8bf qs[NW][QSplit<DK>::QL > 0 ? QSplit<DK>::QL : 1][kWave];  // LDS query part
   int rows[MAX_ROWS];                        // physical row of each selected entry, or -1
 };
 
-// Issue the gather of chunk c (32 rows) into `tile`: wave-load j covers 64 consecutive 16-byte
-// tile slots; lane i fills slot 64j + i (pad slots and slots past the tile get a harmless load
-// of the first chunk of the KV array).
+// Issue the gather of one chunk (32 rows) into `tile`: wave-load j covers 64 consecutive
+// 16-byte tile slots; lane i fills slot 64j + i.  `row` holds, in lane l (and l + 32), the
+// physical row of entry l of the chunk or -1; each lane takes its slot's row from there.
+// Pad slots, slots past the tile and entries that are not valid rows get a harmless load of
+// the first 16 bytes of the KV array (their contents are never used: pad slots are never read
+// and invalid keys are masked out of the softmax).
 template <int DK>
 __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __restrict__ kv,
-                                             const int* rows, int c, int nrows, int wave,
-                                             int lane) {
+                                             int row, int wave, int lane) {
   using T = Tile<DK>;
-  for (int j = wave; j < T::LOADS; j += NW) {
-    const int u = j * kWave + lane;
+  constexpr int GJ = (T::LOADS + NW - 1) / NW;
+  // The slot arithmetic below is the same for every chunk; recomputing it (a few VALU ops)
+  // is cheaper than keeping it live across the loop, so hide the lane id from hoisting.
+  int ln;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+#pragma unroll
+  for (int jj = 0; jj < GJ; ++jj) {
+    const int j = wave + NW * jj;
+    if (GJ * NW > T::LOADS && j >= T::LOADS) break;     // wave-uniform
+    const int u = j * kWave + ln;
     const int r = u / T::SLOTS;
     const int p = u - r * T::SLOTS;
-    const int e = c * CH + r;
-    int row = (r < CH && e < nrows) ? rows[e] : -1;
-    const bool real = row >= 0 && p < T::NCH;
-    const uint16_t* src = real ? kv + (size_t)row * DK + 8 * p : kv;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+    int rw;
+    if constexpr (T::SLOTS >= kWave) {
+      // the wave-load spans at most two rows: two lane reads
+      const int rlo = (j * kWave) / T::SLOTS;           // row of the wave-load's first slot
+      const int ra = __builtin_amdgcn_readlane(row, rlo < CH ? rlo : CH - 1);
+      const int rb = __builtin_amdgcn_readlane(row, rlo + 1 < CH ? rlo + 1 : CH - 1);
+      rw = r == rlo ? ra : rb;
+    } else {
+      rw = __shfl(row, r & (CH - 1));                   // short rows: one lane permute
+    }
+    const bool real = (r < CH) & (rw >= 0) & (p < T::NCH);
+    const size_t off = (size_t)(u32)(real ? rw : 0) * DK + (u32)(real ? 8 * p : 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kv + off),
                                      (__attribute__((address_space(3))) void*)(tile + 16 * kWave * j),
                                      16, 0, 0);
   }
@@ -127,7 +146,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t kt1[Tile<DK>::BYTES];  // selected rows, buffer 1
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler
+                                                                 // keep wave-derived values in SGPRs
   const int hg = wave & 3;          // head group
   const int dh = wave >> 2;         // dimension half
   const int lane = tid & (kWave - 1);
@@ -196,8 +216,18 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   float l_run = 0.f;
 
   const int n_chunks = (nrows + CH - 1) / CH;
+  // physical row of entry c32 of chunk cc, or -1 (entries past the slice included)
+  auto chunk_row = [&](int cc) -> int {
+    const int e = cc * CH + c32;
+    const int v = sh.rows[e < MAX_ROWS ? e : MAX_ROWS - 1];
+    return e < nrows ? v : -1;
+  };
   __syncthreads();   // rows[] complete
-  if (n_chunks > 0) gather_chunk<DK>(kt0, kv, sh.rows, 0, nrows, wave, lane);
+  int row_nx = chunk_row(0);                         // rows of the chunk gathered next
+  if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane);
+  // bit k of vm_cur: key k of the current chunk is a valid selected row
+  u32 vm_cur = (u32)wave_ballot(row_nx >= 0);
+  row_nx = chunk_row(1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -212,7 +242,10 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 
   auto step = [&](const lds_u8* tile, uint8_t* next_tile, int c) {
     // ---- prefetch the next chunk into the other buffer ----
-    if (c + 1 < n_chunks) gather_chunk<DK>(next_tile, kv, sh.rows, c + 1, nrows, wave, lane);
+    if (c + 1 < n_chunks) gather_chunk<DK>(next_tile, kv, row_nx, wave, lane);
+    const u32 vm_nx = (u32)wave_ballot(row_nx >= 0);
+    const u32 vmask = vm_cur;
+    row_nx = chunk_row(c + 2);
 
     // ---- S^T = K Q^T for 32 keys x this wave's 32 heads, over its half of the dims ----
     v16f sp_;
@@ -226,40 +259,49 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       sp_ = mfma_bf16(as_v8bf(av), b, sp_);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sh.sx[wave][i][lane] = sp_[i];
+    for (int i4 = 0; i4 < 4; ++i4)
+      sh.sx[wave][i4][lane] = v4f{sp_[4 * i4], sp_[4 * i4 + 1], sp_[4 * i4 + 2], sp_[4 * i4 + 3]};
     lds_barrier();
 
     // ---- online softmax (lane = head; element i is key 8(i/4) + 4hf + i%4), two passes over
     // the logits in LDS so that only the packed probabilities stay in registers ----
-    // bit k of vmask: key k of the chunk is a valid selected row
-    const int ek = c * CH + c32;
-    const u32 vmask = (u32)wave_ballot(ek < nrows && sh.rows[ek < nrows ? ek : 0] >= 0);
     // masked keys get a -inf bias (loads stay unconditional, no branches)
     float cmax = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
-      const float bias = ((vmask >> key) & 1u) ? 0.f : -__builtin_inff();
-      const float sv = sh.sx[hg][i][lane] + sh.sx[hg + 4][i][lane];
-      cmax = fmaxf(cmax, fmaf(sv, scale_log2, bias));
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const v4f sa = sh.sx[hg][i4][lane], sb = sh.sx[hg + 4][i4][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+        const float bias = ((vmask >> key) & 1u) ? 0.f : -__builtin_inff();
+        cmax = fmaxf(cmax, fmaf(sa[e] + sb[e], scale_log2, bias));
+      }
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool any = m_new != -__builtin_inff();
-    const float m_use = any ? m_new : 0.f;
-    const float alpha = any ? exp2f(m_run - m_new) : 1.f;
+    // Lazy rescaling: the reference max only moves when a logit exceeds it by more than 8
+    // (log2 units), so probabilities stay below 2^8 and the accumulators are rarely rescaled.
+    float alpha = 1.f;
+    if (cmax > m_run + 8.f) {
+      alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - cmax);
+      m_run = cmax;
+    }
+    const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
     float psum = 0.f;
     v8bf pb[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
-      const float bias = ((vmask >> key) & 1u) ? -m_use : -__builtin_inff();
-      const float sv = sh.sx[hg][i][lane] + sh.sx[hg + 4][i][lane];
-      const float pv = exp2f(fmaf(sv, scale_log2, bias));
-      psum += pv;
-      pb[i >> 3][i & 7] = (__bf16)pv;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const v4f sa = sh.sx[hg][i4][lane], sb = sh.sx[hg + 4][i4][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+        const float bias = ((vmask >> key) & 1u) ? -m_use : -__builtin_inff();
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sa[e] + sb[e], scale_log2, bias));
+        psum += pv;
+        pb[i >> 3][i & 7] = (__bf16)pv;
+      }
     }
-    m_run = m_new;
     l_run = l_run * alpha + psum;
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
@@ -283,6 +325,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
         o[d] = mfma_bf16(a, pb[k2], o[d]);
       }
     }
+    vm_cur = vm_nx;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next chunk has landed
     __syncthreads();
   };

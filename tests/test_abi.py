@@ -48,9 +48,10 @@ def test_abi_version_and_status_strings():
 
 def test_workspace_sizes():
     lib = dsa.load_library()
-    # candidate lists: 2*top_k (score, position) pairs per row
-    assert lib.dsa_indexer_topk_workspace_size(4096, 2048) == 4096 * 4096 * 8
-    assert lib.dsa_indexer_topk_workspace_size(16, 32) == 16 * 128 * 8
+    # candidate lists of (score, position) pairs per row: room for top_k kept items plus two
+    # 128-key tiles of appends, at least 2*top_k + 128, rounded up to 128 entries
+    assert lib.dsa_indexer_topk_workspace_size(4096, 2048) == 4096 * 4224 * 8
+    assert lib.dsa_indexer_topk_workspace_size(16, 32) == 16 * 384 * 8
     assert lib.dsa_indexer_topk_workspace_size(-1, 32) == 0
     assert lib.dsa_indexer_topk_paged_workspace_size(64, 2048, 64) == 64 * 2048 * 64 * 4
     # B=64, top_k=2048 -> 4 splits of 512 rows: partial o (fp32) + (max, sum) per head
