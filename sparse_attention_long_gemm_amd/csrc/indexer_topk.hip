@@ -6,18 +6,24 @@
 // under (score desc, position asc).
 //
 // Prefill kernel (one contiguous sequence)
-//   One workgroup owns QB = 16 query rows and streams the keys 0..max(t) of its rows in tiles
-//   of 64.  Each of its 4 waves holds the FP8 queries of 16 indexer heads for all 16 rows in
-//   registers (the MFMA B operand, 8 VGPRs per head) and multiplies them with 16-key FP8
-//   fragments of k_I (A operand) using v_mfma_f32_16x16x128_f8f6f4: the output lane owns one
-//   query row, so ReLU and the head weights are applied and summed in registers with no
-//   cross-lane traffic.  The 4 per-wave partial sums (16 heads each) meet in LDS, where the
-//   causal mask and a per-row threshold filter run; rows' surviving (score, position) items
-//   are appended in position order to a per-row candidate list in the workspace.  When a
-//   list would overflow, it is cut to exactly top_k items by the block-wide radix select
-//   (dsa_select.hpp), which also raises the row's threshold to the top_k-th score; only keys
-//   scoring strictly above it can enter afterwards (a later key with an equal score has a
-//   higher position, so it would lose the tie).  No n_q x L score matrix is ever stored.
+//   One workgroup (8 waves) owns QB = 16 query rows and streams the keys 0..max(t) of its rows,
+//   128 keys per iteration, through a double-buffered LDS key tile (16-byte chunks
+//   XOR-swizzled).  Wave (hg, kh) holds the FP8 queries of indexer heads 16hg..16hg+15 for the
+//   16 rows in registers (the B operand of v_mfma_f32_16x16x128_f8f6f4, 8 VGPRs per head) and
+//   scores the 64 keys of tile half kh: the output lane owns one query row, so the head sum
+//   runs in registers.  ReLU is split as w ReLU(x) = (w x + w |x|) / 2: the |x| half costs one
+//   fma per product (the abs is a free operand modifier), and the linear half is a single
+//   product q_lin . k with q_lin[t] = sum_j w[t,j] q_I[t,j,:], run on bf16 MFMAs with q_lin
+//   split exactly into three bf16 pieces (FP8 keys convert to bf16 exactly).  The per-wave
+//   partial sums meet in LDS, where each wave applies the causal mask and a per-row threshold
+//   filter to its 2 rows and appends the surviving (score, position) items, in position order,
+//   to the row's candidate list in the workspace.  When lists near their capacity, every row
+//   past half of its slack is cut at the next iteration (all waves together) to a threshold
+//   that is at most its top_k-th score: from a per-row LDS histogram of the listed scores when
+//   that leaves enough room, else by an exact radix select (dsa_select.hpp).  Only keys
+//   scoring strictly above the row's threshold can enter afterwards (a later key with an equal
+//   score has a higher position, so it would lose the tie).  A last exact select per row
+//   writes the sorted top_k positions.  No n_q x L score matrix is ever stored.
 //
 // Decode kernels (paged cache, one query per sequence)
 //   indexer_logits_paged: one wave scores 64 keys of one sequence; the A operand is the
