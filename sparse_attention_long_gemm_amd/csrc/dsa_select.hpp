@@ -160,11 +160,9 @@ __device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_
   u32 kand = 0xffffffffu, kor = 0u;
   for (int base = 0; base < n; base += kWave * kSelU) {
     u32 kk[kSelU];
+    // clamped, unconditional loads: all of them are in flight before the first use
 #pragma unroll
-    for (int u = 0; u < kSelU; ++u) {
-      const int i = base + u * kWave + lane;
-      kk[u] = i < n ? key_of(i) : 0u;
-    }
+    for (int u = 0; u < kSelU; ++u) kk[u] = key_of(min(base + u * kWave + lane, n - 1));
 #pragma unroll
     for (int u = 0; u < kSelU; ++u) {
       const bool in = base + u * kWave + lane < n;
@@ -192,10 +190,7 @@ __device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_
       for (int base = 0; base < n; base += kWave * kSelU) {
         u32 kk[kSelU];
 #pragma unroll
-        for (int u = 0; u < kSelU; ++u) {
-          const int i = base + u * kWave + lane;
-          kk[u] = i < n ? key_of(i) : 0u;
-        }
+        for (int u = 0; u < kSelU; ++u) kk[u] = key_of(min(base + u * kWave + lane, n - 1));
 #pragma unroll
         for (int u = 0; u < kSelU; ++u) {
           const bool match = (base + u * kWave + lane < n) && (kk[u] & pmask) == prefix;

@@ -26,11 +26,14 @@
 //   writes the sorted top_k positions.  No n_q x L score matrix is ever stored.
 //
 // Decode kernels (paged cache, one query per sequence)
-//   indexer_logits_paged: one wave scores 64 keys of one sequence; the A operand is the
+//   indexer_logits_paged: one wave scores 1024 keys of one sequence; the A operand is the
 //   query's 64 heads (4 fragments of 16), the B operand 16 keys read through the page table,
-//   so the output lane owns one key and 4 heads; heads are summed in registers and across
-//   the 4 lane groups.  Logits go to the workspace ([B, max_pages*page_size] fp32, 4 bytes
-//   per key against 128 bytes of key read).  topk_rows then selects each row exactly.
+//   so the output lane owns one key and 4 heads; heads are summed in registers and across the
+//   4 lane groups.  Scores go to the workspace (4 bytes per key against 128 bytes of key read)
+//   and into a per-row histogram of their top 12 order-key bits.  The histogram locates the
+//   bin holding the top_k-th score; one pass over the scores, spread over many workgroups
+//   (dec_collect), lists every key above that bin and every key inside it; dec_finish picks
+//   the missing keys exactly among the latter and writes the row in position order.
 #include "dsa_common.hpp"
 #include "dsa_kernels.hpp"
 #include "dsa_select.hpp"
@@ -474,91 +477,549 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode: logits of one query per sequence over its paged keys.
+// Decode: scores of one query per sequence over its paged keys, then an exact row top-k.
+//
+//  1. dec_zero_kernel clears the per-row histograms and list counters.
+//  2. indexer_logits_paged_kernel writes the fp32 scores of keys [0, n) of each row
+//     (n = min(ctx, max_pages * page_size)) and counts them in a per-row histogram of the top
+//     HBITS bits of their order keys (LDS histogram per workgroup, merged with atomics).
+//  3. dec_collect_kernel: the histogram gives the bin b1 that holds the top_k-th best score;
+//     workgroups over slices of the row list the positions of the keys above b1 and the keys
+//     inside b1 (order key, position).
+//  4. dec_finish_kernel, one workgroup per row: marks the keys above b1 in an LDS bitmap over
+//     positions, chooses the missing keys exactly among the candidates (their next 12 key
+//     bits from a histogram, the last 8 from one more pass, then the lowest positions among
+//     keys tied with the threshold) and reads the bitmap out in position order.
 // ------------------------------------------------------------------------------------------
-constexpr int DEC_KEYS_PER_WAVE = 64;
 constexpr int DEC_WAVES = 4;
-constexpr int DEC_KEYS_PER_BLOCK = DEC_KEYS_PER_WAVE * DEC_WAVES;
+constexpr int DEC_NT = DEC_WAVES * kWave;
+constexpr int DEC_WAVE_KEYS = 1024;                          // 16 groups of 64 keys per wave
+constexpr int DEC_BLOCK_KEYS = DEC_WAVES * DEC_WAVE_KEYS;
+constexpr int DEC_NBUF = 2;                                  // key groups in registers
+constexpr int HBITS = 12;                                    // histogram: top 12 key bits
+constexpr int NBIN = 1 << HBITS;
+constexpr int SEL_NT = 1024;
+constexpr int SEL_U = 16;                                    // scores per thread (collect)
+constexpr int COLLECT_CHUNK = SEL_NT * SEL_U;                // scores per collect workgroup
+constexpr int SEL_CAND_LDS = 9216;                           // candidates kept on chip
+constexpr int SEL_BITMAP_WORDS = 8192;                       // rows up to 2^18 positions
+constexpr int kMaxK = 2048;
 
-__global__ __launch_bounds__(DEC_WAVES * kWave) void indexer_logits_paged_kernel(
+__device__ __forceinline__ int hist_bin(u32 key) { return (int)(key >> (32 - HBITS)); }
+
+// Workspace of the paged indexer, carved from one caller buffer (offsets 256-byte aligned).
+struct DecWs {
+  float* logits;     // [B, row_stride]   scores
+  u32* hist;         // [B, NBIN]         histogram of the scores' top HBITS order-key bits
+  int32_t* cnt;      // [B, 4]            list sizes: keys above bin b1, keys in b1
+  int32_t* above;    // [B, kMaxK]        positions of the keys above bin b1
+  u32* cand_key;     // [B, row_stride]   keys in bin b1: order key and position
+  int32_t* cand_pos; // [B, row_stride]
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline size_t dec_ws_layout(int B, int row_stride, DecWs* w, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+  const size_t o_log = take((size_t)B * row_stride * 4);
+  const size_t o_hist = take((size_t)B * NBIN * 4);
+  const size_t o_cnt = take((size_t)B * 4 * 4);
+  const size_t o_above = take((size_t)B * kMaxK * 4);
+  const size_t o_ck = take((size_t)B * row_stride * 4);
+  const size_t o_cp = take((size_t)B * row_stride * 4);
+  if (w != nullptr) {
+    w->logits = reinterpret_cast<float*>(base + o_log);
+    w->hist = reinterpret_cast<u32*>(base + o_hist);
+    w->cnt = reinterpret_cast<int32_t*>(base + o_cnt);
+    w->above = reinterpret_cast<int32_t*>(base + o_above);
+    w->cand_key = reinterpret_cast<u32*>(base + o_ck);
+    w->cand_pos = reinterpret_cast<int32_t*>(base + o_cp);
+  }
+  return off;
+}
+
+__global__ __launch_bounds__(DEC_NT) void dec_zero_kernel(u32* __restrict__ hist,
+                                                          int32_t* __restrict__ cnt) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < NBIN; i += DEC_NT) hist[(size_t)b * NBIN + i] = 0u;
+  if (threadIdx.x < 4) cnt[4 * b + threadIdx.x] = 0;
+}
+
+// n / d for 0 <= n < 2^31 and a divisor d >= 1 fixed for a launch, by one multiply-high
+// (Granlund and Montgomery, "Division by Invariant Integers using Multiplication", 1994):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+  u32 m;
+  u32 l;
+  int d;
+};
+
+inline FastDiv make_fastdiv(int d) {
+  FastDiv f;
+  f.d = d;
+  f.l = 0;
+  while ((1ull << f.l) < (unsigned long long)d) ++f.l;
+  f.m = (u32)((((1ull << 32) * ((1ull << f.l) - (unsigned long long)d)) / (unsigned long long)d) + 1);
+  return f;
+}
+
+__device__ __forceinline__ int fast_div(int n, const FastDiv& f) {
+  return (int)((__umulhi((u32)n, f.m) + (u32)n) >> f.l);
+}
+
+// 16 bytes of an FP8 key row, streamed once: non-temporal load.
+__device__ __forceinline__ v4i load16_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+
+// One workgroup scores DEC_BLOCK_KEYS consecutive keys of one sequence, each wave 16 groups of
+// 64 keys with the next group's loads in flight while a group is computed.  Wave: the A
+// operand is the query's 64 heads (4 fragments of 16 heads x 128 bytes, kept in registers),
+// the B operand 16 keys (lane group g holds bytes [32g, 32g+32) of key c16), so the output
+// lane holds 4 heads of one key; heads are summed in registers and across the 4 lane groups.
+// Keys whose page-table entry is outside [0, n_pages) score as a zero key.  ALIGNED: the page
+// size is a multiple of 64, so each group of 64 keys lies in one page (one uniform lookup).
+template <bool ALIGNED>
+__global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ ctx_lens, int max_pages, int n_pages, int page_size, int H_I,
-    int d_I, int row_stride, float* __restrict__ logits) {
+    const int32_t* __restrict__ ctx_lens, int max_pages, int n_pages, FastDiv page, int H_I,
+    int d_I, int row_stride, float* __restrict__ logits, u32* __restrict__ hist) {
+  const int page_size = page.d;
+  __shared__ u32 lh[NBIN];
   const int b = blockIdx.y;
-  const int ctx = ctx_lens[b];
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
+  const int n = min(max(ctx_lens[b], 0), row_stride);
+  const int blk0 = blockIdx.x * DEC_BLOCK_KEYS;
+  if (blk0 >= n) return;                                     // uniform over the workgroup
+  const int tid = threadIdx.x;
+  for (int i = tid; i < NBIN; i += DEC_NT) lh[i] = 0u;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
   const int g = lane >> 4, c16 = lane & 15;
-  const int base = blockIdx.x * DEC_KEYS_PER_BLOCK + wave * DEC_KEYS_PER_WAVE;
-  if (base >= ctx) return;
+  const int base = blk0 + wave * DEC_WAVE_KEYS;
+  const int ngroups = base < n ? min((n - base + 63) / 64, DEC_WAVE_KEYS / 64) : 0;
+  const int32_t* pt = page_table + (size_t)b * max_pages;
+  const bool lo_ok = 32 * g < d_I, hi_ok = 32 * g + 16 < d_I;
 
-  // A operand: heads 16*hg + (lane & 15), bytes [32g, 32g+32)
+  // keys 64gr + 16f + c16 of the wave: bytes [32g, 32g+32) of each (zero when outside the
+  // context, past d_I or on an invalid page; such lanes load from the start of the cache)
+  auto load_group = [&](int gr, v8i (&kb)[4], u32& okm) {
+    okm = 0u;
+    int gpage = 0, gslot = 0;
+    if (ALIGNED) {
+      const int s0 = base + 64 * gr;                         // uniform
+      const int pi = fast_div(s0, page);
+      gslot = s0 - pi * page_size;
+      gpage = (s0 < n && gr < ngroups) ? pt[pi] : 0;
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int s = base + 64 * gr + 16 * f + c16;
+      const bool in = s < n && gr < ngroups;
+      int pg, slot;
+      if (ALIGNED) {
+        pg = gpage;
+        slot = gslot + 16 * f + c16;
+      } else {
+        const int pi = fast_div(s, page);
+        pg = in ? pt[pi] : 0;
+        slot = s - pi * page_size;
+      }
+      const bool ok = in && pg >= 0 && pg < n_pages;
+      okm |= (ok ? 1u : 0u) << f;
+      const uint8_t* row =
+          k_cache + (ok ? ((size_t)pg * page_size + slot) * d_I : (size_t)0);
+      v4i lo = load16_nt(lo_ok ? row + 32 * g : row);
+      v4i hi = load16_nt(hi_ok ? row + 32 * g + 16 : row);
+      if (!lo_ok) lo = v4i{0, 0, 0, 0};
+      if (!hi_ok) hi = v4i{0, 0, 0, 0};
+      kb[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // DEC_NBUF group buffers: while group gr is computed, groups gr+1 .. gr+DEC_NBUF-1 are in
+  // flight (loads past the wave's keys are harmless reads of the cache start)
+  v8i kbuf[DEC_NBUF][4];
+  u32 okb[DEC_NBUF];
+  if (ngroups > 0) {
+#pragma unroll
+    for (int j = 0; j < DEC_NBUF - 1; ++j) load_group(j, kbuf[j], okb[j]);
+  }
+
+  // query heads 16hg + c16 (A operand) and the head weights of output rows 4g + i
   v8i qa[4];
   float wl[4][4];
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg) {
     const int h = 16 * hg + c16;
-    qa[hg] = load_row32(q_idx + ((size_t)b * H_I + h) * d_I, g, d_I, h < H_I);
+    qa[hg] = load_row32(q_idx + ((size_t)b * H_I + (h < H_I ? h : 0)) * d_I, g, d_I, h < H_I);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * hg + 4 * g + i;  // head of output row 4g+i
+      const int hh = 16 * hg + 4 * g + i;
       wl[hg][i] = (hh < H_I) ? w[(size_t)b * H_I + hh] : 0.f;
     }
   }
-  const int32_t* pt = page_table + (size_t)b * max_pages;
+  __syncthreads();   // lh cleared
+
+  auto compute_group = [&](int gr, const v8i (&kb)[4], u32 okm) {
+    float tot[4];
+    // software-pipelined: the 4 MFMAs of fragment f+1 are issued before the epilogue of f
+    v4f x[4], xn[4];
+    auto frag = [&](int f) {
+      v8i k = kb[f];
+      if (!((okm >> f) & 1u)) k = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      return k;
+    };
+    {
+      const v8i k0 = frag(0);
 #pragma unroll
-  for (int f = 0; f < DEC_KEYS_PER_WAVE / 16; ++f) {
-    const int s = base + 16 * f + c16;
-    bool ok = s < ctx && s < row_stride;
-    int page = 0;
-    if (ok) {
-      page = pt[s / page_size];
-      ok = (page >= 0) && (page < n_pages);
+      for (int hg = 0; hg < 4; ++hg) x[hg] = mfma_fp8(qa[hg], k0);  // heads 16hg+4g+i, key c16
     }
-    const uint8_t* row = k_cache + ((size_t)page * page_size + (ok ? s % page_size : 0)) * d_I;
-    const v8i kb = load_row32(row, g, d_I, ok);
-    float acc = 0.f;
 #pragma unroll
-    for (int hg = 0; hg < 4; ++hg) {
-      const v4f x = mfma_fp8(qa[hg], kb);  // rows: heads 16hg+4g+i, column: key c16
-      acc = fmaf(wl[hg][0], fmaxf(x[0], 0.f), acc);
-      acc = fmaf(wl[hg][1], fmaxf(x[1], 0.f), acc);
-      acc = fmaf(wl[hg][2], fmaxf(x[2], 0.f), acc);
-      acc = fmaf(wl[hg][3], fmaxf(x[3], 0.f), acc);
+    for (int f = 0; f < 4; ++f) {
+      if (f < 3) {
+        const v8i kf = frag(f + 1);
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) xn[hg] = mfma_fp8(qa[hg], kf);
+      }
+      float acc = 0.f;
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) {
+        acc = fmaf(wl[hg][0], fmaxf(x[hg][0], 0.f), acc);
+        acc = fmaf(wl[hg][1], fmaxf(x[hg][1], 0.f), acc);
+        acc = fmaf(wl[hg][2], fmaxf(x[hg][2], 0.f), acc);
+        acc = fmaf(wl[hg][3], fmaxf(x[hg][3], 0.f), acc);
+      }
+      acc += __shfl_xor(acc, 16);
+      acc += __shfl_xor(acc, 32);
+      tot[f] = acc;
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) x[hg] = xn[hg];
     }
-    acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
-    if (g == 0 && s < ctx && s < row_stride) logits[(size_t)b * row_stride + s] = acc;
+    // lane group g keeps key 16g + c16 of the group
+    const float v = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+    const int s = base + 64 * gr + lane;
+    if (s < n && gr < ngroups) {
+      const float sc = v == 0.f ? 0.f : v;
+      logits[(size_t)b * row_stride + s] = sc;
+      atomicAdd(&lh[hist_bin(ord_key(sc))], 1u);
+    }
+  };
+#pragma unroll 1
+  for (int gr = 0; gr < ngroups; gr += DEC_NBUF) {
+#pragma unroll
+    for (int j = 0; j < DEC_NBUF; ++j) {
+      const int nb = (j + DEC_NBUF - 1) % DEC_NBUF;
+      load_group(gr + j + DEC_NBUF - 1, kbuf[nb], okb[nb]);
+      compute_group(gr + j, kbuf[j], okb[j]);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < NBIN; i += DEC_NT) {
+    const u32 c = lh[i];
+    if (c != 0u) atomicAdd(&hist[(size_t)b * NBIN + i], c);
   }
 }
 
-constexpr int TOPK_NT = 1024;
+// The bin of an NB-bin histogram (bins ordered like the keys) that holds the k-th largest
+// key, and the number of keys in higher bins.  Every thread of the block gets the result.
+// Requires at least k counted keys.  h may be in global memory or LDS.
+template <int NT, int NB>
+__device__ void threshold_bin(const u32* h, int k, int* sh_scan, int& bin, int& above) {
+  constexpr int PER = NB >= NT ? NB / NT : 1;
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const bool has = PER * tid < NB;
+  int c[PER];
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = has ? (int)h[PER * tid + i] : 0;
+    tot += c[i];
+  }
+  // inclusive suffix sum over threads >= tid: within the wave, then across waves
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_down(incl, o);
+    if (lane + o < kWave) incl += t;
+  }
+  if (lane == 0) sh_scan[wave] = incl;  // wave total
+  __syncthreads();
+  int after = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) after += (v > wave) ? sh_scan[v] : 0;
+  incl += after;
+  const int excl = incl - tot;   // keys in bins above this thread's range
+  __syncthreads();
+  if (has && excl < k && k <= incl) {
+    int cum = excl;
+    for (int i = PER - 1; i >= 0; --i) {
+      if (cum + c[i] >= k) {
+        sh_scan[NW] = PER * tid + i;
+        sh_scan[NW + 1] = cum;
+        break;
+      }
+      cum += c[i];
+    }
+  }
+  __syncthreads();
+  bin = sh_scan[NW];
+  above = sh_scan[NW + 1];
+}
 
-struct PosItem {
-  u32 key;
-  int32_t pos;
+constexpr int SEL_TIE_LDS = 1024;   // tied candidates ranked on chip
+
+// Order key of a stored score.  The scores in the workspace hold no -0 (the logits kernel
+// stores +0 for it), so the sign-flip form agrees with ord_key.
+__device__ __forceinline__ u32 stored_key(float v) {
+  const u32 u = __float_as_uint(v);
+  return u ^ ((u32)((int)u >> 31) | 0x80000000u);
+}
+
+// One pass over a slice of the row's scores (COLLECT_CHUNK per workgroup): positions of keys
+// above bin b1 go to the row's `above` list, keys inside b1 (order key, position) to its
+// candidate list.  List space is reserved with one atomic per workgroup and list (device-wide
+// atomics on one address serialise, so they are kept few).
+__global__ __launch_bounds__(SEL_NT) void dec_collect_kernel(const int32_t* __restrict__ ctx_lens,
+                                                             int row_stride, int top_k,
+                                                             DecWs ws) {
+  constexpr int NW = SEL_NT / kWave;
+  __shared__ int sh_scan[NW + 2];
+  __shared__ int sh_cnt[2][NW];
+  __shared__ int sh_base[2];
+  const int b = blockIdx.y;
+  const int n = min(max(ctx_lens[b], 0), row_stride);
+  const int base = blockIdx.x * COLLECT_CHUNK;
+  if (n <= top_k || base >= n) return;                       // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const float* row = ws.logits + (size_t)b * row_stride;
+  // clamped, unconditional loads, in flight while the histogram is scanned
+  float v[SEL_U];
+#pragma unroll
+  for (int u = 0; u < SEL_U; ++u) v[u] = row[min(base + u * SEL_NT + tid, n - 1)];
+  int b1, above;
+  threshold_bin<SEL_NT, NBIN>(ws.hist + (size_t)b * NBIN, top_k, sh_scan, b1, above);
+  u32 key[SEL_U];
+  int na = 0, nc = 0;
+#pragma unroll
+  for (int u = 0; u < SEL_U; ++u) {
+    const bool in = base + u * SEL_NT + tid < n;
+    key[u] = stored_key(v[u]);
+    const int bin = hist_bin(key[u]);
+    na += __builtin_popcountll(wave_ballot(in && bin > b1));
+    nc += __builtin_popcountll(wave_ballot(in && bin == b1));
+  }
+  const int wave = tid / kWave;
+  if (lane == 0) {
+    sh_cnt[0][wave] = na;
+    sh_cnt[1][wave] = nc;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    int t = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) t += sh_cnt[tid][v];
+    sh_base[tid] = t > 0 ? atomicAdd(&ws.cnt[4 * b + tid], t) : 0;
+  }
+  __syncthreads();
+  int pa = sh_base[0], pc = sh_base[1];
+  for (int v = 0; v < wave; ++v) {
+    pa += sh_cnt[0][v];
+    pc += sh_cnt[1][v];
+  }
+  int32_t* al = ws.above + (size_t)b * kMaxK;
+  u32* ck = ws.cand_key + (size_t)b * row_stride;
+  int32_t* cp = ws.cand_pos + (size_t)b * row_stride;
+#pragma unroll
+  for (int u = 0; u < SEL_U; ++u) {
+    const int i = base + u * SEL_NT + tid;
+    const bool in = i < n;
+    const int bin = hist_bin(key[u]);
+    const bool ab = in && bin > b1, ca = in && bin == b1;
+    const uint64_t ma = wave_ballot(ab), mc = wave_ballot(ca);
+    if (ab) {
+      const int q = pa + lanes_below(ma);
+      if (q < kMaxK) al[q] = i;
+    }
+    if (ca) {
+      const int q = pc + lanes_below(mc);
+      ck[q] = key[u];
+      cp[q] = i;
+    }
+    pa += __builtin_popcountll(ma);
+    pc += __builtin_popcountll(mc);
+  }
+  (void)above;
+}
+
+struct FinShared {
+  SelectShared sel;
+  int scan[SEL_NT / kWave + 2];
+  int n_list;
+  int n_tie;
+  u32 bitmap[SEL_BITMAP_WORDS];   // selected positions (rows up to 2^18 keys)
+  int32_t list[kMaxK];            // selected positions of longer rows (sorted at the end)
+  u32 hsub[NBIN];                 // histogram of candidate key bits 19..8, then 7..0
+  int32_t tie[SEL_TIE_LDS];       // positions of the candidates equal to the threshold
+  u32 ck[SEL_CAND_LDS];           // candidates staged on chip (the rest read from global)
+  int32_t cp[SEL_CAND_LDS];
 };
 
-__global__ __launch_bounds__(TOPK_NT) void topk_rows_kernel(const float* __restrict__ logits,
-                                                            const int32_t* __restrict__ ctx_lens,
-                                                            int row_stride, int top_k,
+// One workgroup per row: the keys above bin b1 are selected; the missing ones are chosen
+// exactly among the candidates in b1, then the row is written in position order.
+__global__ __launch_bounds__(SEL_NT) void dec_finish_kernel(const int32_t* __restrict__ ctx_lens,
+                                                            int row_stride, int top_k, DecWs ws,
                                                             int32_t* __restrict__ out_idx) {
-  __shared__ SelectShared sh;
+  __shared__ FinShared sh;
   const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int n = min(max(ctx_lens[b], 0), row_stride);
-  const float* row = logits + (size_t)b * row_stride;
   int32_t* orow = out_idx + (size_t)b * top_k;
   if (n <= top_k) {
-    for (int i = threadIdx.x; i < top_k; i += TOPK_NT) orow[i] = (i < n) ? i : -1;
+    for (int i = tid; i < top_k; i += SEL_NT) orow[i] = (i < n) ? i : -1;
     return;
   }
-  u32 T;
-  int r;
-  block_radix_select<TOPK_NT>([&](int i) { return ord_key(row[i]); }, n, top_k, sh, T, r);
-  block_stable_keep<TOPK_NT>(
-      [&](int i) { PosItem it; it.key = ord_key(row[i]); it.pos = i; return it; }, n, T, r,
-      [&](const PosItem& it, int p) { if (p < top_k) orow[p] = it.pos; }, sh);
+  int b1, above;
+  threshold_bin<SEL_NT, NBIN>(ws.hist + (size_t)b * NBIN, top_k, sh.scan, b1, above);
+  const int c = ws.cnt[4 * b + 1];                 // candidates in bin b1
+  const bool use_bitmap = n <= SEL_BITMAP_WORDS * 32;
+  const int n_words = (n + 31) / 32;
+  if (use_bitmap)
+    for (int i = tid; i < n_words; i += SEL_NT) sh.bitmap[i] = 0u;
+  for (int i = tid; i < NBIN; i += SEL_NT) sh.hsub[i] = 0u;
+  if (tid == 0) { sh.n_list = 0; sh.n_tie = 0; }
+  __syncthreads();
+  auto mark = [&](int pos) {
+    if (use_bitmap) {
+      atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
+    } else {
+      const int p = atomicAdd(&sh.n_list, 1);
+      if (p < kMaxK) sh.list[p] = pos;
+    }
+  };
+  const u32* gck = ws.cand_key + (size_t)b * row_stride;
+  const int32_t* gcp = ws.cand_pos + (size_t)b * row_stride;
+  // keys above b1; the candidates staged on chip, with the histogram of their bits 19..8
+  const int32_t* al = ws.above + (size_t)b * kMaxK;
+  for (int i = tid; i < above; i += SEL_NT) mark(al[i]);
+  for (int i = tid; i < c; i += SEL_NT) {
+    const u32 k = gck[i];
+    const int32_t p = gcp[i];
+    if (i < SEL_CAND_LDS) {
+      sh.ck[i] = k;
+      sh.cp[i] = p;
+    }
+    atomicAdd(&sh.hsub[(k >> 8) & (NBIN - 1)], 1u);
+  }
+  __syncthreads();
+  const int need = top_k - above;                  // >= 1 keys to take from bin b1
+  auto ckey = [&](int i) -> u32 { return i < SEL_CAND_LDS ? sh.ck[i] : gck[i]; };
+  auto cpos = [&](int i) -> int32_t { return i < SEL_CAND_LDS ? sh.cp[i] : gcp[i]; };
+
+  // ---- the need-th largest candidate key T (candidates share key bits 31..20): bits 19..8
+  // from the histogram, bits 7..0 from one more pass ----
+  u32 T = 0u, TP = 0u;
+  const bool all = c <= need;
+  if (!all) {
+    int d2, above2, d3, above3;
+    threshold_bin<SEL_NT, NBIN>(sh.hsub, need, sh.scan, d2, above2);
+    const int need2 = need - above2;
+    for (int i = tid; i < 256; i += SEL_NT) sh.hsub[i] = 0u;
+    __syncthreads();
+    const u32 pre = ((u32)b1 << 20) | ((u32)d2 << 8);
+    for (int i = tid; i < c; i += SEL_NT) {
+      const u32 k = ckey(i);
+      if ((k & 0xffffff00u) == pre) atomicAdd(&sh.hsub[k & 255u], 1u);
+    }
+    __syncthreads();
+    threshold_bin<SEL_NT, 256>(sh.hsub, need2, sh.scan, d3, above3);
+    T = pre | (u32)d3;
+    const int r = need2 - above3;                  // keys equal to T to take (>= 1)
+    const int n_eq = (int)sh.hsub[d3];
+    if (n_eq > r) {
+      // ties at T: take the r lowest positions
+      if (n_eq <= SEL_TIE_LDS) {
+        for (int i = tid; i < c; i += SEL_NT) {
+          if (ckey(i) == T) sh.tie[atomicAdd(&sh.n_tie, 1)] = cpos(i);
+        }
+        __syncthreads();
+        // the r-th lowest tied position: the one with exactly r - 1 lower ones
+        for (int i = tid; i < n_eq; i += SEL_NT) {
+          const int pi = sh.tie[i];
+          int lower = 0;
+          for (int j = 0; j < n_eq; ++j) lower += sh.tie[j] < pi ? 1 : 0;
+          if (lower == r - 1) sh.scan[0] = pi;
+        }
+        __syncthreads();
+        TP = ~(u32)sh.scan[0];
+      } else {
+        int r2;
+        block_radix_select<SEL_NT>(
+            [&](int i) { return ckey(i) == T ? ~(u32)cpos(i) : 0u; }, c, r, sh.sel, TP, r2);
+      }
+    }
+  }
+  for (int i = tid; i < c; i += SEL_NT) {
+    const u32 k = ckey(i);
+    if (all || k > T || (k == T && ~(u32)cpos(i) >= TP)) mark(cpos(i));
+  }
+  __syncthreads();
+
+  // ---- the selected positions in ascending order ----
+  if (use_bitmap) {
+    constexpr int WPT = SEL_BITMAP_WORDS / SEL_NT;
+    const int w0 = tid * WPT;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) cnt += w0 + j < n_words ? __builtin_popcount(sh.bitmap[w0 + j]) : 0;
+    // exclusive prefix over threads
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) sh.scan[wave] = incl;
+    __syncthreads();
+    int off = incl - cnt;
+    for (int v = 0; v < wave; ++v) off += sh.scan[v];
+#pragma unroll 1
+    for (int j = 0; j < WPT; ++j) {
+      if (w0 + j >= n_words) break;
+      u32 bits = sh.bitmap[w0 + j];
+      while (bits != 0u) {
+        const int bit = __builtin_ctz(bits);
+        if (off < top_k) orow[off] = 32 * (w0 + j) + bit;
+        ++off;
+        bits &= bits - 1u;
+      }
+    }
+  } else {
+    // bitonic sort of the listed positions, padded to a power of two
+    int N = 1;
+    while (N < top_k) N <<= 1;
+    for (int i = top_k + tid; i < N; i += SEL_NT) sh.list[i] = 0x7fffffff;
+    __syncthreads();
+    for (int k2 = 2; k2 <= N; k2 <<= 1) {
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < N; i += SEL_NT) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const int a = sh.list[i], d = sh.list[ixj];
+            const bool up = (i & k2) == 0;
+            if ((a > d) == up) {
+              sh.list[i] = d;
+              sh.list[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < top_k; i += SEL_NT) orow[i] = sh.list[i];
+  }
 }
 
 }  // namespace
@@ -591,7 +1052,7 @@ hipError_t launch_indexer_topk_prefill(const uint8_t* q_idx, const float* w, con
 }
 
 size_t indexer_paged_ws(int B, int max_pages, int page_size) {
-  return (size_t)B * (size_t)max_pages * (size_t)page_size * sizeof(float);
+  return dec_ws_layout(B, max_pages * page_size, nullptr, nullptr);
 }
 
 hipError_t launch_indexer_topk_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_cache,
@@ -599,15 +1060,28 @@ hipError_t launch_indexer_topk_paged(const uint8_t* q_idx, const float* w, const
                                      int max_pages, int n_pages, int page_size, int H_I, int d_I,
                                      int top_k, int32_t* out_idx, void* ws, hipStream_t stream) {
   const int row_stride = max_pages * page_size;
-  float* logits = reinterpret_cast<float*>(ws);
-  dim3 grid((row_stride + DEC_KEYS_PER_BLOCK - 1) / DEC_KEYS_PER_BLOCK, B);
-  hipLaunchKernelGGL(indexer_logits_paged_kernel, grid, dim3(DEC_WAVES * kWave), 0, stream, q_idx,
-                     w, k_cache, page_table, ctx_lens, max_pages, n_pages, page_size, H_I, d_I,
-                     row_stride, logits);
+  DecWs d;
+  dec_ws_layout(B, row_stride, &d, reinterpret_cast<char*>(ws));
+  hipLaunchKernelGGL(dec_zero_kernel, dim3(B), dim3(DEC_NT), 0, stream, d.hist, d.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(B), dim3(TOPK_NT), 0, stream, logits, ctx_lens,
-                     row_stride, top_k, out_idx);
+  dim3 grid((row_stride + DEC_BLOCK_KEYS - 1) / DEC_BLOCK_KEYS, B);
+  const FastDiv pdiv = make_fastdiv(page_size);
+  if (page_size % 64 == 0)
+    hipLaunchKernelGGL(indexer_logits_paged_kernel<true>, grid, dim3(DEC_NT), 0, stream, q_idx,
+                       w, k_cache, page_table, ctx_lens, max_pages, n_pages, pdiv, H_I, d_I,
+                       row_stride, d.logits, d.hist);
+  else
+    hipLaunchKernelGGL(indexer_logits_paged_kernel<false>, grid, dim3(DEC_NT), 0, stream, q_idx,
+                       w, k_cache, page_table, ctx_lens, max_pages, n_pages, pdiv, H_I, d_I,
+                       row_stride, d.logits, d.hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  dim3 cgrid((row_stride + COLLECT_CHUNK - 1) / COLLECT_CHUNK, B);
+  hipLaunchKernelGGL(dec_collect_kernel, cgrid, dim3(SEL_NT), 0, stream, ctx_lens, row_stride,
+                     top_k, d);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dec_finish_kernel, dim3(B), dim3(SEL_NT), 0, stream, ctx_lens, row_stride,
+                     top_k, d, out_idx);
   return hipGetLastError();
 }
 

@@ -53,7 +53,11 @@ def test_workspace_sizes():
     assert lib.dsa_indexer_topk_workspace_size(4096, 2048) == 4096 * 4224 * 8
     assert lib.dsa_indexer_topk_workspace_size(16, 32) == 16 * 384 * 8
     assert lib.dsa_indexer_topk_workspace_size(-1, 32) == 0
-    assert lib.dsa_indexer_topk_paged_workspace_size(64, 2048, 64) == 64 * 2048 * 64 * 4
+    # paged: per key slot an fp32 score and a candidate (order key, position); per row a
+    # 4096-bin histogram, 4 counters and a 2048-entry list (each part 256-byte aligned)
+    rs = 2048 * 64
+    assert lib.dsa_indexer_topk_paged_workspace_size(64, 2048, 64) == \
+        3 * 64 * rs * 4 + 64 * 4096 * 4 + 1024 + 64 * 2048 * 4
     # B=64, top_k=2048 -> 4 splits of 512 rows: partial o (fp32) + (max, sum) per head
     assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 2048, 0) == 64 * 4 * 128 * 514 * 4
     assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 2048, 1) == 0

@@ -276,14 +276,19 @@ def run_decode(d, n_split=0):
     return idx, o, lse
 
 
-@pytest.mark.parametrize("page_size,top_k,ctx,n_split", [
-    (64, 2048, (4096, 5000, 2100, 9000), 0),
-    (64, 256, (300, 64, 1, 1000, 777), 0),
-    (16, 512, (513, 2000, 100), 3),
-    (64, 2048, (2047, 2048, 2049, 130), 1),
+@pytest.mark.parametrize("page_size,top_k,ctx,n_split,small_idx", [
+    (64, 2048, (4096, 5000, 2100, 9000), 0, False),
+    (64, 256, (300, 64, 1, 1000, 777), 0, False),
+    (16, 512, (513, 2000, 100), 3, False),
+    (64, 2048, (2047, 2048, 2049, 130), 1, False),
+    (32, 64, (3000, 65, 700), 0, True),     # H_I = 4, d_I = 32: partial MFMA operands
 ])
-def test_decode_small(page_size, top_k, ctx, n_split):
-    sp = gi.DecodeSpec(B=len(ctx), page_size=page_size, idx=gi.IndexerSpec(top_k=top_k),
+def test_decode_small(page_size, top_k, ctx, n_split, small_idx):
+    ix = gi.IndexerSpec(top_k=top_k)
+    if small_idx:
+        ix = gi.IndexerSpec(H_I=4, d_I=32, grid_lo=-3, grid_hi=3, grid_step=0.125,
+                            w_choices=(0.25, 0.5, 1.0), top_k=top_k)
+    sp = gi.DecodeSpec(B=len(ctx), page_size=page_size, idx=ix,
                        mqa=gi.MqaSpec(sigma=1.0), spare_pages=5, seed=21)
     d = gi.decode_inputs(sp, ctx_lens=ctx)
     step(f"decode P={page_size} k={top_k} ctx={ctx} split={n_split}")
@@ -292,6 +297,22 @@ def test_decode_small(page_size, top_k, ctx, n_split):
     i_ref, o_ref, l_ref = orc.decode(d)
     check_idx(idx, i_ref, "decode idx")
     check_attn(o, lse, o_ref, l_ref, "decode attn")
+
+
+def test_decode_ties_large_candidate_list():
+    """All scores of sequence 0 tie (zero query): the threshold bin holds every key, more than
+    the selection stages on chip, so the exact tie-break runs over the whole list."""
+    sp = gi.DecodeSpec(B=3, idx=gi.IndexerSpec(top_k=2048), mqa=gi.MqaSpec(sigma=1.0), seed=29)
+    d = gi.decode_inputs(sp, ctx_lens=(20000, 5000, 13000))
+    d["q_idx"][0].zero_()
+    d["w"][2] = -d["w"][2]          # all scores <= 0: the selection runs over non-positive keys
+    step("decode ties / large candidate list")
+    idx, o, lse = run_decode(d)
+    torch.cuda.synchronize()
+    i_ref, o_ref, l_ref = orc.decode(d)
+    assert np.array_equal(i_ref[0], np.arange(2048))
+    check_idx(idx, i_ref, "decode ties idx")
+    check_attn(o, lse, o_ref, l_ref, "decode ties attn")
 
 
 def test_decode_equals_prefill_last_row():
