@@ -153,21 +153,59 @@ namespace dsa {
 // ------------------------------------------------------------------------------------------
 constexpr int kSelU = 16;
 
+// Batch loaders for wave_radix_select: load(base, kk, in) fills the order keys of items
+// base .. base + 64 kSelU - 1 (any order) and whether each is below n.  Every load of a batch
+// is issued before any of them is used.
 template <class KeyOf>
-__device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_out, int& r_out) {
+struct ScalarKeys {
+  KeyOf key_of;
+  int n;
+  __device__ void operator()(int base, u32 (&kk)[kSelU], bool (&in)[kSelU]) const {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) kk[u] = key_of(min(base + u * kWave + lane, n - 1));
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) in[u] = base + u * kWave + lane < n;
+  }
+};
+
+// fp32 scores stored contiguously (16-byte aligned, readable up to the next multiple of 4
+// items): 16-byte loads, 4 items per load, so a batch takes kSelU / 4 loads per lane.
+struct ScoreKeys {
+  const float* cs;
+  int n;
+  __device__ void operator()(int base, u32 (&kk)[kSelU], bool (&in)[kSelU]) const {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int V = kSelU / 4;
+    const int last = (n - 1) & ~3;                    // last 4-aligned item index below n
+    v4f f[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      f[v] = *reinterpret_cast<const v4f*>(cs + min(base + 256 * v + 4 * lane, last));
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kk[4 * v + e] = ord_key(f[v][e]);
+        in[4 * v + e] = base + 256 * v + 4 * lane + e < n;
+      }
+  }
+};
+
+template <class Loader>
+__device__ void wave_radix_select_batched(const Loader& load, int n, int k, u32* hist, u32& T_out,
+                                          int& r_out) {
   const int lane = threadIdx.x & (kWave - 1);
   // bits on which all keys agree need no pass
   u32 kand = 0xffffffffu, kor = 0u;
   for (int base = 0; base < n; base += kWave * kSelU) {
     u32 kk[kSelU];
-    // clamped, unconditional loads: all of them are in flight before the first use
-#pragma unroll
-    for (int u = 0; u < kSelU; ++u) kk[u] = key_of(min(base + u * kWave + lane, n - 1));
+    bool in[kSelU];
+    load(base, kk, in);
 #pragma unroll
     for (int u = 0; u < kSelU; ++u) {
-      const bool in = base + u * kWave + lane < n;
-      kand &= in ? kk[u] : 0xffffffffu;
-      kor |= in ? kk[u] : 0u;
+      kand &= in[u] ? kk[u] : 0xffffffffu;
+      kor |= in[u] ? kk[u] : 0u;
     }
   }
   for (int o = 32; o >= 1; o >>= 1) {
@@ -189,11 +227,11 @@ __device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       for (int base = 0; base < n; base += kWave * kSelU) {
         u32 kk[kSelU];
-#pragma unroll
-        for (int u = 0; u < kSelU; ++u) kk[u] = key_of(min(base + u * kWave + lane, n - 1));
+        bool in[kSelU];
+        load(base, kk, in);
 #pragma unroll
         for (int u = 0; u < kSelU; ++u) {
-          const bool match = (base + u * kWave + lane < n) && (kk[u] & pmask) == prefix;
+          const bool match = in[u] && (kk[u] & pmask) == prefix;
           const u32 d = (kk[u] >> shift) & dmask;
           const uint64_t mm = wave_ballot(match);
           if (mm == 0ull) continue;
@@ -247,6 +285,20 @@ __device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_
   }
   T_out = prefix;
   r_out = remaining;
+}
+
+// Step 1 for one wave: the k-th largest order key T among items 0..n-1 (n > k >= 1) and the
+// number r of items equal to T that belong to the top k.  key_of(i) returns the ord_key of
+// item i.
+template <class KeyOf>
+__device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_out, int& r_out) {
+  wave_radix_select_batched(ScalarKeys<KeyOf>{key_of, n}, n, k, hist, T_out, r_out);
+}
+
+// Step 1 over fp32 scores stored contiguously (see ScoreKeys).
+__device__ inline void wave_radix_select_scores(const float* cs, int n, int k, u32* hist,
+                                                u32& T_out, int& r_out) {
+  wave_radix_select_batched(ScoreKeys{cs, n}, n, k, hist, T_out, r_out);
 }
 
 // Wave-level stable keep (see block_stable_keep).  All U chunks of a batch are loaded before

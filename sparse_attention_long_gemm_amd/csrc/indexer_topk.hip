@@ -172,7 +172,7 @@ __device__ float wave_cut(float* cs, int32_t* ci, int n, int top_k, int cap, u32
     }
   }
   int r = 0;
-  if (exact) wave_radix_select([&](int i) { return ord_key(cs[i]); }, n, top_k, hist, T, r);
+  if (exact) wave_radix_select_scores(cs, n, top_k, hist, T, r);
   // rebuild the histogram for the survivors over [T, hi_seen]
 #pragma unroll
   for (int b = 0; b < 4; ++b) rh[4 * lane + b] = 0u;
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     } else {
       u32 T;
       int r;
-      wave_radix_select([&](int i) { return ord_key(cs[i]); }, n, top_k, sh.hist[wave], T, r);
+      wave_radix_select_scores(cs, n, top_k, sh.hist[wave], T, r);
       wave_stable_keep(
           [&](int i) { CandItem it; it.score = cs[i]; it.pos = ci[i]; it.key = ord_key(it.score); return it; },
           n, T, r, [&](const CandItem& it, int p) { if (p < top_k) orow[p] = it.pos; });
