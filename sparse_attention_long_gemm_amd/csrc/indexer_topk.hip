@@ -26,7 +26,7 @@
 //   writes the sorted top_k positions.  No n_q x L score matrix is ever stored.
 //
 // Decode kernels (paged cache, one query per sequence)
-//   indexer_logits_paged: one wave scores 1024 keys of one sequence; the A operand is the
+//   indexer_logits_paged: one wave scores 256 keys of one sequence; the A operand is the
 //   query's 64 heads (4 fragments of 16), the B operand 16 keys read through the page table,
 //   so the output lane owns one key and 4 heads; heads are summed in registers and across the
 //   4 lane groups.  Scores go to the workspace (4 bytes per key against 128 bytes of key read)
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 // ------------------------------------------------------------------------------------------
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_NT = DEC_WAVES * kWave;
-constexpr int DEC_WAVE_KEYS = 1024;                          // 16 groups of 64 keys per wave
+constexpr int DEC_WAVE_KEYS = 256;                           // 4 groups of 64 keys per wave
 constexpr int DEC_BLOCK_KEYS = DEC_WAVES * DEC_WAVE_KEYS;
 constexpr int DEC_NBUF = 2;                                  // key groups in registers
 constexpr int HBITS = 12;                                    // histogram: top 12 key bits
@@ -573,8 +573,9 @@ __device__ __forceinline__ v4i load16_nt(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
-// One workgroup scores DEC_BLOCK_KEYS consecutive keys of one sequence, each wave 16 groups of
-// 64 keys with the next group's loads in flight while a group is computed.  Wave: the A
+// One workgroup scores DEC_BLOCK_KEYS consecutive keys of one sequence, each wave 4 groups of
+// 64 keys with the next group's loads in flight while a group is computed (small workgroups
+// keep the machine evenly loaded across sequences of very different lengths).  Wave: the A
 // operand is the query's 64 heads (4 fragments of 16 heads x 128 bytes, kept in registers),
 // the B operand 16 keys (lane group g holds bytes [32g, 32g+32) of key c16), so the output
 // lane holds 4 heads of one key; heads are summed in registers and across the 4 lane groups.
@@ -608,10 +609,11 @@ __global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
     okm = 0u;
     int gpage = 0, gslot = 0;
     if (ALIGNED) {
-      const int s0 = base + 64 * gr;                         // uniform
-      const int pi = fast_div(s0, page);
+      // uniform: one scalar load of the group's page (index clamped into the row's table)
+      const int s0 = base + 64 * gr;
+      const int pi = fast_div(min(s0, n - 1), page);
       gslot = s0 - pi * page_size;
-      gpage = (s0 < n && gr < ngroups) ? pt[pi] : 0;
+      gpage = pt[pi < max_pages ? pi : max_pages - 1];
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -630,10 +632,8 @@ __global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
       okm |= (ok ? 1u : 0u) << f;
       const uint8_t* row =
           k_cache + (ok ? ((size_t)pg * page_size + slot) * d_I : (size_t)0);
-      v4i lo = load16_nt(lo_ok ? row + 32 * g : row);
-      v4i hi = load16_nt(hi_ok ? row + 32 * g + 16 : row);
-      if (!lo_ok) lo = v4i{0, 0, 0, 0};
-      if (!hi_ok) hi = v4i{0, 0, 0, 0};
+      const v4i lo = load16_nt(lo_ok ? row + 32 * g : row);
+      const v4i hi = load16_nt(hi_ok ? row + 32 * g + 16 : row);
       kb[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
@@ -665,9 +665,14 @@ __global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
     float tot[4];
     // software-pipelined: the 4 MFMAs of fragment f+1 are issued before the epilogue of f
     v4f x[4], xn[4];
+    // bytes past d_I are zeroed here, at the use (short rows only: a uniform branch), so the
+    // loads stay in flight until the MFMA needs them
     auto frag = [&](int f) {
       v8i k = kb[f];
-      if (!((okm >> f) & 1u)) k = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      if (d_I < 128) {
+        if (!lo_ok) k[0] = k[1] = k[2] = k[3] = 0;
+        if (!hi_ok) k[4] = k[5] = k[6] = k[7] = 0;
+      }
       return k;
     };
     {
@@ -682,22 +687,23 @@ __global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
 #pragma unroll
         for (int hg = 0; hg < 4; ++hg) xn[hg] = mfma_fp8(qa[hg], kf);
       }
-      float acc = 0.f;
+      // four independent chains (one per output row of the fragment), summed at the end
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hg = 0; hg < 4; ++hg) {
-        acc = fmaf(wl[hg][0], fmaxf(x[hg][0], 0.f), acc);
-        acc = fmaf(wl[hg][1], fmaxf(x[hg][1], 0.f), acc);
-        acc = fmaf(wl[hg][2], fmaxf(x[hg][2], 0.f), acc);
-        acc = fmaf(wl[hg][3], fmaxf(x[hg][3], 0.f), acc);
-      }
+      for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a4[i] = fmaf(wl[hg][i], fmaxf(x[hg][i], 0.f), a4[i]);
+      float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
       acc += __shfl_xor(acc, 16);
       acc += __shfl_xor(acc, 32);
       tot[f] = acc;
 #pragma unroll
       for (int hg = 0; hg < 4; ++hg) x[hg] = xn[hg];
     }
-    // lane group g keeps key 16g + c16 of the group
-    const float v = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+    // lane group g keeps key 16g + c16 of the group; a key on an invalid page scores as a
+    // zero key (0)
+    float v = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+    if (!((okm >> g) & 1u)) v = 0.f;
     const int s = base + 64 * gr + lane;
     if (s < n && gr < ngroups) {
       const float sc = v == 0.f ? 0.f : v;
