@@ -480,9 +480,10 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 // Decode: scores of one query per sequence over its paged keys, then an exact row top-k.
 //
 //  1. dec_zero_kernel clears the per-row histograms and list counters.
-//  2. indexer_logits_paged_kernel writes the fp32 scores of keys [0, n) of each row
-//     (n = min(ctx, max_pages * page_size)) and counts them in a per-row histogram of the top
-//     HBITS bits of their order keys (LDS histogram per workgroup, merged with atomics).
+//  2. indexer_logits_paged_kernel (persistent, equal shares of all rows' keys per wave) writes
+//     the fp32 scores of keys [0, n) of each row (n = min(ctx, max_pages * page_size)) and
+//     counts them in a per-row histogram of the top HBITS bits of their order keys (LDS
+//     histogram per wave, merged with atomics).
 //  3. dec_collect_kernel: the histogram gives the bin b1 that holds the top_k-th best score;
 //     workgroups over slices of the row list the positions of the keys above b1 and the keys
 //     inside b1 (order key, position).
@@ -493,9 +494,15 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 // ------------------------------------------------------------------------------------------
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_NT = DEC_WAVES * kWave;
-constexpr int DEC_WAVE_KEYS = 256;                           // 4 groups of 64 keys per wave
-constexpr int DEC_BLOCK_KEYS = DEC_WAVES * DEC_WAVE_KEYS;
-constexpr int DEC_NBUF = 2;                                  // key groups in registers
+constexpr int DEC_UNIT = 32;                                 // keys per scoring unit
+constexpr int DEC_UNIT_LOADS = DEC_UNIT * 128 / 1024;        // wave-loads per unit
+constexpr int DEC_NBUF = 2;                                  // units in LDS per wave
+constexpr int DEC_WG_PER_CU = 1;                             // scoring workgroups per CU
+constexpr int SC_WAVES = 8;                                  // waves per scoring workgroup
+constexpr int SC_NT = SC_WAVES * kWave;
+// per-wave histogram counts are 16 bits (two bins per LDS word): flushed at least every
+// HIST16_UNITS units so that no count can carry into its neighbour
+constexpr int HIST16_UNITS = 65535 / DEC_UNIT - 1;
 constexpr int HBITS = 12;                                    // histogram: top 12 key bits
 constexpr int NBIN = 1 << HBITS;
 constexpr int SEL_NT = 1024;
@@ -573,102 +580,215 @@ __device__ __forceinline__ v4i load16_nt(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
-// One workgroup scores DEC_BLOCK_KEYS consecutive keys of one sequence, each wave 4 groups of
-// 64 keys with the next group's loads in flight while a group is computed (small workgroups
-// keep the machine evenly loaded across sequences of very different lengths).  Wave: the A
-// operand is the query's 64 heads (4 fragments of 16 heads x 128 bytes, kept in registers),
-// the B operand 16 keys (lane group g holds bytes [32g, 32g+32) of key c16), so the output
-// lane holds 4 heads of one key; heads are summed in registers and across the 4 lane groups.
-// Keys whose page-table entry is outside [0, n_pages) score as a zero key.  ALIGNED: the page
-// size is a multiple of 64, so each group of 64 keys lies in one page (one uniform lookup).
+// Persistent streaming scorer.  The keys of all rows are cut into units of DEC_UNIT
+// consecutive positions (row b has ceil(n_b / DEC_UNIT) units); every wave of the grid takes
+// an equal contiguous range of the flattened unit list, so rows of very different lengths load
+// the machine evenly and each wave keeps DEC_NBUF - 1 units of loads in flight for its whole
+// life instead of ramping up and down with short-lived workgroups.  The keys go straight from
+// memory into a per-wave LDS ring (global_load_lds, 16 bytes per lane): 8 lanes cover one
+// whole 128-byte key row, so each wave-load asks the memory system for 8 full cache lines (the
+// per-CU limit on outstanding requests, not their size, bounds the stream, so full-line
+// requests and 8 scoring waves per CU both count).  Waves are independent: each has its own
+// LDS ring and its own LDS histogram (16-bit counts) of the row it is on, flushed into the
+// row's global histogram (bins it touched only) when it moves to the next row, before a count
+// could overflow, and at its end.
+// Unit compute: the A operand is the row's query, 64 heads (4 fragments of 16 heads x 128
+// bytes, kept in registers), the B operand 16 keys (lane group g holds bytes [32g, 32g+32)
+// of key c16, read from the ring), so the output lane holds 4 heads of one key; heads are
+// summed in registers and across the 4 lane groups.  Keys whose page-table entry is outside
+// [0, n_pages) score as a zero key.  ALIGNED: the page size is a multiple of DEC_UNIT, so a
+// unit lies in one page (one uniform lookup).
 template <bool ALIGNED>
-__global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
+__global__ __launch_bounds__(SC_NT) void indexer_logits_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ ctx_lens, int max_pages, int n_pages, FastDiv page, int H_I,
-    int d_I, int row_stride, float* __restrict__ logits, u32* __restrict__ hist) {
+    const int32_t* __restrict__ ctx_lens, int B, int max_pages, int n_pages, FastDiv page,
+    int H_I, int d_I, int row_stride, float* __restrict__ logits, u32* __restrict__ hist) {
   const int page_size = page.d;
-  __shared__ u32 lh[NBIN];
-  const int b = blockIdx.y;
-  const int n = min(max(ctx_lens[b], 0), row_stride);
-  const int blk0 = blockIdx.x * DEC_BLOCK_KEYS;
-  if (blk0 >= n) return;                                     // uniform over the workgroup
+  __shared__ u32 lh_all[SC_WAVES][NBIN / 2];   // two 16-bit bins per word
+  // ring slot of chunk c (16 bytes) of key k of a unit: 8k + (c ^ ((k >> 1) & 7)); the swizzle
+  // puts the 16 keys of an operand read on distinct LDS banks
+  __shared__ __attribute__((aligned(16))) uint8_t ring_all[SC_WAVES][DEC_NBUF][DEC_UNIT * 128];
   const int tid = threadIdx.x;
-  for (int i = tid; i < NBIN; i += DEC_NT) lh[i] = 0u;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid & (kWave - 1);
   const int g = lane >> 4, c16 = lane & 15;
-  const int base = blk0 + wave * DEC_WAVE_KEYS;
-  const int ngroups = base < n ? min((n - base + 63) / 64, DEC_WAVE_KEYS / 64) : 0;
-  const int32_t* pt = page_table + (size_t)b * max_pages;
+  u32* lh = lh_all[wave];
   const bool lo_ok = 32 * g < d_I, hi_ok = 32 * g + 16 < d_I;
 
-  // keys 64gr + 16f + c16 of the wave: bytes [32g, 32g+32) of each (zero when outside the
-  // context, past d_I or on an invalid page; such lanes load from the start of the cache)
-  auto load_group = [&](int gr, v8i (&kb)[4], u32& okm) {
-    okm = 0u;
+  // keys of row bb that are scored, and its unit count
+  auto row_len = [&](int bb) { return min(max(ctx_lens[bb], 0), row_stride); };
+
+  // ---- this wave's unit range [u0, u1) of the flattened list, and the row / unit it starts in
+  auto units = [&](int bb) -> long long {
+    return bb < B ? (row_len(bb) + DEC_UNIT - 1) / DEC_UNIT : 0;
+  };
+  long long total = 0;
+  for (int b0 = 0; b0 < B; b0 += kWave) {
+    long long u = units(b0 + lane);
+    for (int o = 32; o >= 1; o >>= 1) u += __shfl_xor(u, o);
+    total += u;
+  }
+  const long long n_waves = (long long)gridDim.x * SC_WAVES;
+  const long long gw = (long long)blockIdx.x * SC_WAVES + wave;
+  const long long u0 = total * gw / n_waves, u1 = total * (gw + 1) / n_waves;
+  // (the reductions above leave the same value in every lane; make that visible to the
+  // compiler so the loop control and the row cursors below live in scalar registers)
+  const int my_units = __builtin_amdgcn_readfirstlane((int)(u1 - u0));
+  int cb = 0, cj = 0;   // row and unit of u0
+  if (my_units > 0) {
+    long long before = 0;
+    for (int b0 = 0; b0 < B; b0 += kWave) {
+      const long long mine = units(b0 + lane);
+      long long incl = mine;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const long long t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const uint64_t hit = wave_ballot(before + incl > u0);
+      if (hit != 0) {
+        const int l = __builtin_ctzll(hit);
+        const long long excl = __shfl(incl - mine, l);
+        cb = b0 + l;
+        cj = (int)(u0 - before - excl);
+        break;
+      }
+      before += __shfl(incl, kWave - 1);
+    }
+  }
+  cb = __builtin_amdgcn_readfirstlane(cb);
+  cj = __builtin_amdgcn_readfirstlane(cj);
+
+  // A cursor over the unit list: row b (n keys, nu units), unit j of the row.
+  struct Cursor {
+    int b, j, n, nu;
+  };
+  auto cursor_at = [&](int b, int j) {
+    Cursor c;
+    c.b = b;
+    c.j = j;
+    c.n = b < B ? row_len(b) : 0;
+    c.nu = (c.n + DEC_UNIT - 1) / DEC_UNIT;
+    return c;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.j >= c.nu) {
+      c.j = 0;
+      do {
+        ++c.b;
+        c.n = c.b < B ? row_len(c.b) : 0;
+        c.nu = (c.n + DEC_UNIT - 1) / DEC_UNIT;
+      } while (c.b < B && c.nu == 0);
+    }
+  };
+
+  // DMA of unit (c.b, c.j) into ring buffer nb: wave-load jj fills slots 64jj .. 64jj + 63,
+  // i.e. lane l brings chunk (l % 8) ^ ((k >> 1) & 7) of key k = 8jj + l / 8.  Keys outside
+  // the context or on an invalid page, chunks past d_I and every lane of a unit past the
+  // wave's range load 16 harmless bytes from the start of the cache (masked or zeroed at
+  // use).  Returns (uniform) whether the unit's page is valid (ALIGNED only; otherwise the
+  // page is looked up again per key at use).
+  auto dma_unit = [&](const Cursor& c, bool live, int nb) -> bool {
+    const int32_t* pt = page_table + (size_t)(live ? c.b : 0) * max_pages;
     int gpage = 0, gslot = 0;
     if (ALIGNED) {
-      // uniform: one scalar load of the group's page (index clamped into the row's table)
-      const int s0 = base + 64 * gr;
-      const int pi = fast_div(min(s0, n - 1), page);
+      const int s0 = DEC_UNIT * c.j;
+      const int pi = fast_div(min(s0, max(c.n - 1, 0)), page);
       gslot = s0 - pi * page_size;
-      gpage = pt[pi < max_pages ? pi : max_pages - 1];
+      gpage = live ? pt[pi < max_pages ? pi : max_pages - 1] : 0;
     }
+    const u32 lds0 = (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(ring_all[wave][nb]);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int s = base + 64 * gr + 16 * f + c16;
-      const bool in = s < n && gr < ngroups;
+    for (int jj = 0; jj < DEC_UNIT_LOADS; ++jj) {
+      const int k = 8 * jj + (lane >> 3);
+      const int ch = (lane & 7) ^ ((k >> 1) & 7);
+      const int s = DEC_UNIT * c.j + k;
+      const bool in = live && s < c.n && 16 * ch < d_I;
       int pg, slot;
       if (ALIGNED) {
         pg = gpage;
-        slot = gslot + 16 * f + c16;
+        slot = gslot + k;
       } else {
-        const int pi = fast_div(s, page);
+        const int pi = fast_div(in ? s : 0, page);
         pg = in ? pt[pi] : 0;
         slot = s - pi * page_size;
       }
       const bool ok = in && pg >= 0 && pg < n_pages;
-      okm |= (ok ? 1u : 0u) << f;
-      const uint8_t* row =
-          k_cache + (ok ? ((size_t)pg * page_size + slot) * d_I : (size_t)0);
-      const v4i lo = load16_nt(lo_ok ? row + 32 * g : row);
-      const v4i hi = load16_nt(hi_ok ? row + 32 * g + 16 : row);
-      kb[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const uint8_t* src = k_cache + (ok ? ((size_t)pg * page_size + slot) * d_I + 16 * ch : (size_t)0);
+      // written out so that the compiler does not count it as an outstanding LDS access
+      // (its waits are the explicit ones before each unit's use)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                   :
+                   : "v"(src), "s"(lds0 + 1024 * jj)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
     }
+    return !ALIGNED || (gpage >= 0 && gpage < n_pages);
   };
-  // DEC_NBUF group buffers: while group gr is computed, groups gr+1 .. gr+DEC_NBUF-1 are in
-  // flight (loads past the wave's keys are harmless reads of the cache start)
-  v8i kbuf[DEC_NBUF][4];
-  u32 okb[DEC_NBUF];
-  if (ngroups > 0) {
-#pragma unroll
-    for (int j = 0; j < DEC_NBUF - 1; ++j) load_group(j, kbuf[j], okb[j]);
-  }
 
-  // query heads 16hg + c16 (A operand) and the head weights of output rows 4g + i
+  // query heads 16hg + c16 of row qb (A operand) and the head weights of output rows 4g + i
   v8i qa[4];
   float wl[4][4];
+  auto load_query = [&](int qb) {
 #pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-    const int h = 16 * hg + c16;
-    qa[hg] = load_row32(q_idx + ((size_t)b * H_I + (h < H_I ? h : 0)) * d_I, g, d_I, h < H_I);
+    for (int hg = 0; hg < 4; ++hg) {
+      const int h = 16 * hg + c16;
+      qa[hg] = load_row32(q_idx + ((size_t)qb * H_I + (h < H_I ? h : 0)) * d_I, g, d_I, h < H_I);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * hg + 4 * g + i;
-      wl[hg][i] = (hh < H_I) ? w[(size_t)b * H_I + hh] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int hh = 16 * hg + 4 * g + i;
+        wl[hg][i] = (hh < H_I) ? w[(size_t)qb * H_I + hh] : 0.f;
+      }
     }
-  }
-  __syncthreads();   // lh cleared
+    // wait here (once per row) so that no query load is outstanding inside the unit loop: the
+    // in-order load counter would otherwise make every unit's first product wait for the
+    // units still in flight behind it
+    __builtin_amdgcn_s_waitcnt(0);
+  };
 
-  auto compute_group = [&](int gr, const v8i (&kb)[4], u32 okm) {
-    float tot[4];
+  // this wave's histogram: cleared once, then only the touched bin range [bmin, bmax] is
+  // flushed and cleared again
+#pragma unroll
+  for (int i = 0; i < NBIN / 2 / kWave; ++i) lh[i * kWave + lane] = 0u;
+  int bmin = NBIN, bmax = -1;
+  auto flush = [&](int fb) {
+    int lo = bmin, hi = bmax;
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo = min(lo, __shfl_xor(lo, o));
+      hi = max(hi, __shfl_xor(hi, o));
+    }
+    for (int i = (lo >> 1) + lane; i <= (hi >> 1); i += kWave) {   // two bins per word
+      const u32 cnt = lh[i];
+      if (cnt != 0u) {
+        if (cnt & 0xffffu) atomicAdd(&hist[(size_t)fb * NBIN + 2 * i], cnt & 0xffffu);
+        if (cnt >> 16) atomicAdd(&hist[(size_t)fb * NBIN + 2 * i + 1], cnt >> 16);
+        lh[i] = 0u;
+      }
+    }
+    bmin = NBIN;
+    bmax = -1;
+  };
+
+  // lane's ring offsets of chunks 2g and 2g+1 of key c16 of fragment 0 (fragment f: + 2048 f)
+  static_assert(DEC_UNIT % 16 == 0 && DEC_UNIT <= 64, "unit size");
+  const int hsw = (c16 >> 1) & 7;
+  const int rd0 = 128 * c16 + 16 * ((2 * g) ^ hsw), rd1 = 128 * c16 + 16 * ((2 * g + 1) ^ hsw);
+  auto compute_unit = [&](const Cursor& c, int nb, bool page_ok) {
+    const __attribute__((address_space(3))) uint8_t* rb =
+        (const __attribute__((address_space(3))) uint8_t*)ring_all[wave][nb];
+    constexpr int NF = DEC_UNIT / 16;   // 16-key fragments per unit
+    float tot[NF];
     // software-pipelined: the 4 MFMAs of fragment f+1 are issued before the epilogue of f
     v4f x[4], xn[4];
     // bytes past d_I are zeroed here, at the use (short rows only: a uniform branch), so the
     // loads stay in flight until the MFMA needs them
     auto frag = [&](int f) {
-      v8i k = kb[f];
+      const v4i lo = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(rb + rd0 + 2048 * f);
+      const v4i hi = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(rb + rd1 + 2048 * f);
+      v8i k = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       if (d_I < 128) {
         if (!lo_ok) k[0] = k[1] = k[2] = k[3] = 0;
         if (!hi_ok) k[4] = k[5] = k[6] = k[7] = 0;
@@ -681,8 +801,8 @@ __global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
       for (int hg = 0; hg < 4; ++hg) x[hg] = mfma_fp8(qa[hg], k0);  // heads 16hg+4g+i, key c16
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if (f < 3) {
+    for (int f = 0; f < NF; ++f) {
+      if (f < NF - 1) {
         const v8i kf = frag(f + 1);
 #pragma unroll
         for (int hg = 0; hg < 4; ++hg) xn[hg] = mfma_fp8(qa[hg], kf);
@@ -700,31 +820,78 @@ __global__ __launch_bounds__(DEC_NT) void indexer_logits_paged_kernel(
 #pragma unroll
       for (int hg = 0; hg < 4; ++hg) x[hg] = xn[hg];
     }
-    // lane group g keeps key 16g + c16 of the group; a key on an invalid page scores as a
-    // zero key (0)
-    float v = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
-    if (!((okm >> g) & 1u)) v = 0.f;
-    const int s = base + 64 * gr + lane;
-    if (s < n && gr < ngroups) {
+    // lane group g keeps key 16g + c16 of the unit; a key on an invalid page scores as a zero
+    // key (0)
+    float v = tot[0];
+#pragma unroll
+    for (int f = 1; f < NF; ++f) v = g == f ? tot[f] : v;
+    const int s = DEC_UNIT * c.j + lane;
+    bool ok = page_ok;
+    if (!ALIGNED && lane < DEC_UNIT && s < c.n) {
+      const int32_t* pt = page_table + (size_t)c.b * max_pages;
+      const int pg = pt[fast_div(s, page)];
+      ok = pg >= 0 && pg < n_pages;
+    }
+    if (!ok) v = 0.f;
+    if (lane < DEC_UNIT && s < c.n) {
       const float sc = v == 0.f ? 0.f : v;
-      logits[(size_t)b * row_stride + s] = sc;
-      atomicAdd(&lh[hist_bin(ord_key(sc))], 1u);
+      logits[(size_t)c.b * row_stride + s] = sc;
+      const int bin = hist_bin(ord_key(sc));
+      atomicAdd(&lh[bin >> 1], 1u << (16 * (bin & 1)));
+      bmin = min(bmin, bin);
+      bmax = max(bmax, bin);
     }
   };
-#pragma unroll 1
-  for (int gr = 0; gr < ngroups; gr += DEC_NBUF) {
+
+  if (my_units <= 0) return;
+  Cursor lc = cursor_at(cb, cj);   // next unit to load
+  Cursor cc = lc;                  // next unit to compute
+  load_query(cc.b);
+  // DEC_NBUF ring buffers: while unit i is computed, units i+1 .. i+DEC_NBUF-1 are in flight
+  bool pok[DEC_NBUF];
+  int since_flush = 0;   // units counted since the last flush
 #pragma unroll
-    for (int j = 0; j < DEC_NBUF; ++j) {
-      const int nb = (j + DEC_NBUF - 1) % DEC_NBUF;
-      load_group(gr + j + DEC_NBUF - 1, kbuf[nb], okb[nb]);
-      compute_group(gr + j, kbuf[j], okb[j]);
+  for (int r = 0; r < DEC_NBUF - 1; ++r) {
+    pok[r] = dma_unit(lc, r < my_units, r);
+    if (r < my_units) advance(lc);
+  }
+  // wait until at most the newest (DEC_NBUF - 1) units' 8 wave-loads each are outstanding
+  // (vmcnt bits 3:0 and 15:14, expcnt and lgkmcnt left at their no-wait values)
+  constexpr int kVm = DEC_UNIT_LOADS * (DEC_NBUF - 1);
+  constexpr int kWaitUnit = (kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll 1
+  for (int i = 0; i < my_units; i += DEC_NBUF) {
+#pragma unroll
+    for (int r = 0; r < DEC_NBUF; ++r) {
+      const int nb = (r + DEC_NBUF - 1) % DEC_NBUF;
+      const bool live = i + r + DEC_NBUF - 1 < my_units;
+      pok[nb] = dma_unit(lc, live, nb);
+      if (live) advance(lc);
+      if (i + r < my_units) {
+        __builtin_amdgcn_s_waitcnt(kWaitUnit);   // unit i + r has landed in buffer r
+        compute_unit(cc, r, pok[r]);
+        const int ob = cc.b;
+        advance(cc);
+        ++since_flush;
+        if (cc.b != ob) {          // next row: flush this one, fetch the next query
+          flush(ob);
+          since_flush = 0;
+          if (i + r + 1 < my_units) load_query(cc.b);
+        } else if (since_flush >= HIST16_UNITS) {
+          flush(ob);
+          since_flush = 0;
+        }
+      }
     }
   }
-  __syncthreads();
-  for (int i = tid; i < NBIN; i += DEC_NT) {
-    const u32 c = lh[i];
-    if (c != 0u) atomicAdd(&hist[(size_t)b * NBIN + i], c);
-  }
+  flush(cc.b);   // the row of the last unit, unless already flushed (then a no-op)
+}
+
+// Order key of a stored score.  The scores in the workspace hold no -0 (the logits kernel
+// stores +0 for it), so the sign-flip form agrees with ord_key.
+__device__ __forceinline__ u32 stored_key(float v) {
+  const u32 u = __float_as_uint(v);
+  return u ^ ((u32)((int)u >> 31) | 0x80000000u);
 }
 
 // The bin of an NB-bin histogram (bins ordered like the keys) that holds the k-th largest
@@ -776,12 +943,6 @@ __device__ void threshold_bin(const u32* h, int k, int* sh_scan, int& bin, int& 
 
 constexpr int SEL_TIE_LDS = 1024;   // tied candidates ranked on chip
 
-// Order key of a stored score.  The scores in the workspace hold no -0 (the logits kernel
-// stores +0 for it), so the sign-flip form agrees with ord_key.
-__device__ __forceinline__ u32 stored_key(float v) {
-  const u32 u = __float_as_uint(v);
-  return u ^ ((u32)((int)u >> 31) | 0x80000000u);
-}
 
 // One pass over a slice of the row's scores (COLLECT_CHUNK per workgroup): positions of keys
 // above bin b1 go to the row's `above` list, keys inside b1 (order key, position) to its
@@ -1071,15 +1232,20 @@ hipError_t launch_indexer_topk_paged(const uint8_t* q_idx, const float* w, const
   hipLaunchKernelGGL(dec_zero_kernel, dim3(B), dim3(DEC_NT), 0, stream, d.hist, d.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((row_stride + DEC_BLOCK_KEYS - 1) / DEC_BLOCK_KEYS, B);
+  // persistent scorer: a fixed number of workgroups per CU of the current device
+  int dev = 0, n_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  const dim3 grid(DEC_WG_PER_CU * (n_cu > 0 ? n_cu : 1));
   const FastDiv pdiv = make_fastdiv(page_size);
-  if (page_size % 64 == 0)
-    hipLaunchKernelGGL(indexer_logits_paged_kernel<true>, grid, dim3(DEC_NT), 0, stream, q_idx,
-                       w, k_cache, page_table, ctx_lens, max_pages, n_pages, pdiv, H_I, d_I,
+  if (page_size % DEC_UNIT == 0)
+    hipLaunchKernelGGL(indexer_logits_paged_kernel<true>, grid, dim3(SC_NT), 0, stream, q_idx,
+                       w, k_cache, page_table, ctx_lens, B, max_pages, n_pages, pdiv, H_I, d_I,
                        row_stride, d.logits, d.hist);
   else
-    hipLaunchKernelGGL(indexer_logits_paged_kernel<false>, grid, dim3(DEC_NT), 0, stream, q_idx,
-                       w, k_cache, page_table, ctx_lens, max_pages, n_pages, pdiv, H_I, d_I,
+    hipLaunchKernelGGL(indexer_logits_paged_kernel<false>, grid, dim3(SC_NT), 0, stream, q_idx,
+                       w, k_cache, page_table, ctx_lens, B, max_pages, n_pages, pdiv, H_I, d_I,
                        row_stride, d.logits, d.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 cgrid((row_stride + COLLECT_CHUNK - 1) / COLLECT_CHUNK, B);

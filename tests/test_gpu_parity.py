@@ -282,6 +282,7 @@ def run_decode(d, n_split=0):
     (16, 512, (513, 2000, 100), 3, False),
     (64, 2048, (2047, 2048, 2049, 130), 1, False),
     (32, 64, (3000, 65, 700), 0, True),     # H_I = 4, d_I = 32: partial MFMA operands
+    (64, 128, (0, 200, 0, 70, 64), 0, False),  # empty rows between scored ones
 ])
 def test_decode_small(page_size, top_k, ctx, n_split, small_idx):
     ix = gi.IndexerSpec(top_k=top_k)
