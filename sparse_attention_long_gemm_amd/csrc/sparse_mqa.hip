@@ -6,24 +6,23 @@
 // MLA run in MQA mode); only the selected entries are attended (jdon.com "DeepSeek-V3.2-Exp"
 // article, paragraph on fine-grained token selection).
 //
-// One workgroup = one query row (all heads) x one slice of its selected rows, 8 waves.  Wave
-// (hg, dh) owns heads 32hg..32hg+31 and half dh of the dimensions: its share of the queries
-// (dims [D_k/2 * dh, +D_k/2)) stays in registers as the B operand of
-// v_mfma_f32_32x32x16_bf16 and its fp32 output accumulators (dims [D_v/2 * dh, +D_v/2)) stay in
-// registers for the whole slice.  The selected rows are gathered 32 at a time straight from
-// global memory into a double-buffered LDS tile (global_load_lds, 16 bytes per lane; the next
-// chunk's loads are interleaved with the current chunk's logit product).  The tile is
-// row-major with one 16-byte pad per row and the rows of each 16-row half permuted
-// (tile_row), which puts both read patterns on disjoint LDS banks while keeping every address
-// base + constant; it is the A operand of S^T = K Q^T as is, and the A operand of
-// O^T += V^T P^T is read from the same tile with the transposing LDS read (ds_read_b64_tr_b16),
-// so no transposed copy is stored.  The two waves of a head group add their half-dimension
-// partial logits through LDS (in a fixed order, so both hold the same sums).  With keys on the
-// MFMA rows, each lane owns one head, so the online-softmax row max and sum stay in the lane
-// (plus one exchange with the partner lane that holds the other 16 keys), and the
-// probabilities already sit in the B-operand layout of the value product once packed to bf16.
-// The probabilities are formed in one pass against a lazily moved reference max; a chunk is
-// redone in two passes only when one of its logits breaks the bound.
+// One workgroup = one query row (all heads) x one slice of its selected rows, 8 waves.  Wave w
+// owns heads 16w .. 16w+15 over all dimensions (v_mfma_f32_16x16x32_bf16): its queries stay
+// in registers as the B operand of S^T = K Q^T (the last k-steps in LDS) and its fp32 output
+// accumulators O^T stay in registers for the whole slice, so the waves never exchange partial
+// results and every probability is computed once.  The selected rows are gathered 32 at a
+// time straight from global memory into a ring of three LDS tiles (global_load_lds, 16 bytes
+// per lane; two chunks' loads are in flight while one is computed, interleaved with the logit
+// product); the waves meet once per chunk.  The tile is row-major with two 16-byte pad slots
+// per row, which keeps both read patterns free of LDS bank conflicts and every address base +
+// constant; it is the A operand of S^T = K Q^T as is, and the A operand of O^T += V^T P^T is
+// read from the same tile with the transposing LDS read (ds_read_b64_tr_b16), so no
+// transposed copy is stored.  With keys on the MFMA rows, each lane holds 8 keys of one head;
+// the head's row max and sum need one exchange among its 4 lanes, and the probabilities
+// already sit in the B-operand layout of the value product once packed to bf16 (the k slots
+// of that product follow the lane's own keys).  The probabilities are formed in one pass
+// against a lazily moved reference max; a chunk is redone in two passes only when one of its
+// logits breaks the bound.
 //
 // Decode (paged) splits each sequence's selected rows over n_split workgroups; partial
 // (unnormalised o, running max, running sum) triples are merged by mqa_combine_kernel.
@@ -36,12 +35,12 @@ namespace dsa {
 
 namespace {
 
-constexpr int NW = 8;            // 4 head groups x 2 dimension halves
+constexpr int NW = 8;            // waves: 16 heads each, all dimensions
 constexpr int NT = NW * kWave;
-constexpr int HPW = 32;          // heads per wave
+constexpr int HPW = 16;          // heads per wave
 constexpr int CH = 32;           // selected rows per chunk
 constexpr int MAX_ROWS = 2048;   // selected rows per workgroup (top_k <= 2048)
-constexpr int QPD = 3;           // logit-product operands in flight per wave
+constexpr int QPD = 2;           // k-steps of logit operands in flight
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -49,69 +48,15 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 __device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 
-// Workgroup barrier that orders LDS traffic only: it does not wait for outstanding global
-// loads, so the asynchronous gather of the next chunk stays in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ v8bf as_v8bf(const v4i& x) {
   v8bf r;
   __builtin_memcpy(&r, &x, 16);
   return r;
 }
 
-template <int DK>
-struct Tile {
-  static constexpr int NCH = DK / 8;                   // 16-byte chunks of a row
-  static constexpr int SLOTS = NCH + 1;                // + one pad slot
-  static constexpr int RS = 16 * SLOTS;                // row stride (bytes)
-  static constexpr int LOADS = (CH * SLOTS + kWave - 1) / kWave;  // wave-loads per chunk
-  static constexpr int GJ = (LOADS + NW - 1) / NW;                 // of them, per wave
-  static constexpr int BYTES = LOADS * kWave * 16;
-};
-
-// Query fragments of the last QL k-steps of each wave live in LDS instead of registers (this
-// keeps the 576-wide instance within 256 VGPRs per wave at 2 waves per SIMD).
-template <int DK>
-struct QSplit {
-  static constexpr int NKS = DK / 32;
-  static constexpr int QL = NKS >= 16 ? 4 : 0;
-  static constexpr int QR = NKS - QL;
-};
-
-// (The two row-tile buffers are separate __shared__ objects: reads of one buffer then provably
-// do not alias the asynchronous fill of the other, so no wait for that fill is inserted.)
-template <int DK>
-struct MqaShared {
-  alignas(16) v4f sx[NW][4][kWave];          // half-dimension partial logits of each wave:
-                                             // [wave][i/4][lane] holds elements 4(i/4)..+3
-  alignas(16) v8bf qs[NW][QSplit<DK>::QL > 0 ? QSplit<DK>::QL : 1][kWave];  // LDS query part
-  int rows[MAX_ROWS];                        // physical row of each selected entry, or -1
-};
-
-// Tile row of chunk entry e (and entry of tile row e: the map is its own inverse): inside each
-// half of 16 rows, the 4x4 blocks (e = 4a + b -> 4b + a) are transposed.  The logit product
-// reads entries 0..15 (16 lanes per LDS cycle) and the transposing value read reads entries
-// 4a..4a+3 together; with a row stride of 73 16-byte slots, the permuted rows put both
-// groups on disjoint LDS banks (unpermuted, the value read hits 2-way bank conflicts).
-__host__ __device__ constexpr int tile_row(int e) {
-  return (e & ~15) | ((e & 3) << 2) | ((e >> 2) & 3);
-}
-
-// Issue the gather of one chunk (32 rows) into `tile`: wave-load j covers 64 consecutive
-// 16-byte tile slots; lane i fills slot 64j + i.  `row` holds, in lane l (and l + 32), the
-// physical row of entry l of the chunk or -1; each lane takes its slot's row (that of entry
-// tile_row(slot row)) from there.
-// Pad slots, slots past the tile and entries that are not valid rows get a harmless load of
-// the first 16 bytes of the KV array (their contents are never used: pad slots are never read
-// and invalid keys are masked out of the softmax).
-// Wave-load jj of a wave's part of the next chunk's gather is issued after logit product
-// gather_slot(jj) of the current chunk: evenly from the first product to the last but one.
+// Wave-load jj of a wave's part of a chunk's gather is issued after logit product
+// gather_slot(jj) of the chunk computed two steps earlier: evenly from the first product to
+// the last but one.
 template <int NKS, int GJ>
 __device__ constexpr int gather_slot(int jj) {
   return GJ > 1 ? jj * (NKS > 2 ? NKS - 2 : 0) / (GJ - 1) : 0;
@@ -123,17 +68,53 @@ __device__ constexpr int first_load_at(int ks) {   // first wave-load issued aft
   return jj;
 }
 
-// Wave-loads jj0 <= jj < jj1 of this wave (compile-time constants at every call once the
-// caller's loop is unrolled).  A chunk's gather is issued in parts spread over the logit
-// product of the previous chunk, so that the CU's outstanding-miss capacity is not exceeded at
-// once: a load that finds it full stalls its wave at issue.
+
+// Row tile of the head-split kernel: rows in entry order, two 16-byte pad slots per row.  For
+// these read patterns (16 rows x one 16-byte column per lane group for the logit product, two
+// 4-row x 32-byte groups per 32 lanes for the transposing value read) a stride of 74 slots
+// measures free of LDS bank conflicts on gfx950 (73 slots conflicts on the logit read).
+template <int DK>
+struct Tile {
+  static constexpr int NCH = DK / 8;
+  static constexpr int SLOTS = NCH + 2;
+  static constexpr int RS = 16 * SLOTS;
+  static constexpr int LOADS = (CH * SLOTS + kWave - 1) / kWave;
+  static constexpr int BYTES = LOADS * kWave * 16;
+  static constexpr int GJ = (LOADS + NW - 1) / NW;
+};
+
+__device__ __forceinline__ v4f mfma16_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int DK>
+struct QSplit {
+  static constexpr int NKS = DK / 32;
+  static constexpr int QL = NKS >= 16 ? 4 : 0;   // k-steps of the queries kept in LDS
+  static constexpr int QR = NKS - QL;
+};
+
+template <int DK>
+struct MqaShared {
+  alignas(16) v8bf qs[NW][QSplit<DK>::QL > 0 ? QSplit<DK>::QL : 1][kWave];
+  int rows[MAX_ROWS];   // physical row of each selected entry, or -1
+};
+
+// Issue wave-loads jj0 <= jj < jj1 (compile-time constants once the caller's loop is unrolled)
+// of this wave's part of one chunk's gather into `tile`: wave-load j = wave + NW jj covers 64
+// consecutive 16-byte tile slots, lane i filling slot 64j + i.  `row` holds, in lane l (and
+// l + 32), the physical row of entry l of the chunk or -1; each lane takes its slot's row from
+// there.  Pad slots, slots past the tile and entries that are not valid rows get a harmless
+// load of the first 16 bytes of the KV array (pad slots are never read; invalid keys are
+// masked out of the softmax).  The load is written out (global_load_lds_dwordx4: 16 bytes
+// per lane into LDS at M0 + 16 * lane) so that the compiler does not count it as an
+// outstanding LDS access, which would make it wait for all LDS traffic wherever a tile read
+// is consumed; its waits are the explicit ones at the end of each chunk.
 template <int DK>
 __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __restrict__ kv,
                                              int row, int wave, int lane, int jj0, int jj1) {
   using T = Tile<DK>;
   constexpr int GJ = T::GJ;
-  // The slot arithmetic below is the same for every chunk; recomputing it (a few VALU ops)
-  // is cheaper than keeping it live across the loop, so hide the lane id from hoisting.
   int ln;
   asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
 #pragma unroll
@@ -146,21 +127,15 @@ __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __re
     const int p = u - r * T::SLOTS;
     int rw;
     if constexpr (T::SLOTS >= kWave) {
-      // the wave-load spans at most two rows: two lane reads
-      const int rlo = (j * kWave) / T::SLOTS;           // row of the wave-load's first slot
-      const int ra = __builtin_amdgcn_readlane(row, tile_row(rlo < CH ? rlo : CH - 1));
-      const int rb = __builtin_amdgcn_readlane(row, tile_row(rlo + 1 < CH ? rlo + 1 : CH - 1));
+      const int rlo = (j * kWave) / T::SLOTS;
+      const int ra = __builtin_amdgcn_readlane(row, rlo < CH ? rlo : CH - 1);
+      const int rb = __builtin_amdgcn_readlane(row, rlo + 1 < CH ? rlo + 1 : CH - 1);
       rw = r == rlo ? ra : rb;
     } else {
-      rw = __shfl(row, tile_row(r & (CH - 1)));         // short rows: one lane permute
+      rw = __shfl(row, r & (CH - 1));
     }
     const bool real = (r < CH) & (rw >= 0) & (p < T::NCH);
     const size_t off = (size_t)(u32)(real ? rw : 0) * DK + (u32)(real ? 8 * p : 0);
-    // Written out (global_load_lds_dwordx4: 16 bytes per lane into LDS at M0 + 16 * lane) so
-    // that the compiler does not count it as an outstanding LDS access: it would then wait
-    // for all LDS traffic (lgkmcnt(0)) wherever a tile read is consumed instead of only for
-    // that read.  It has no register result; its waits are the explicit full ones that end
-    // each step (and the prologue).
     const u32 lds = (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(tile + 16 * kWave * j);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -172,6 +147,20 @@ __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __re
   }
 }
 
+// Number of wave-loads of one chunk's gather that wave `wave` issues.
+template <int DK>
+__device__ constexpr int gather_count(int wave) {
+  using T = Tile<DK>;
+  int n = 0;
+  for (int jj = 0; jj < T::GJ; ++jj) n += (wave + NW * jj < T::LOADS) ? 1 : 0;
+  return n;
+}
+
+// s_waitcnt immediate: vmcnt = n, expcnt and lgkmcnt not waited for.
+__host__ __device__ constexpr int vm_wait_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 template <int DK, int DV, bool PAGED>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -180,32 +169,29 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     int H, int top_k, float scale_log2, int n_split, int rows_per_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  static_assert(DK % 32 == 0 && DV % 64 == 0 && DV <= DK, "shape");
+  static_assert(DK % 32 == 0 && DV % 16 == 0 && DV <= DK, "shape");
   using Sh = MqaShared<DK>;
-  constexpr int NKS = DK / 32;           // k-steps of this wave's half of the S^T product
-  constexpr int NDB = DV / 64;           // 32-dim blocks of this wave's half of the output
+  constexpr int NKS = DK / 32;           // k-steps of the S^T product
+  constexpr int NDB = DV / 16;           // 16-dim blocks of the output
   constexpr int RS = Tile<DK>::RS;
   constexpr int GJ = Tile<DK>::GJ;
+  constexpr int QR = QSplit<DK>::QR;
   __shared__ Sh sh;
-  __shared__ __attribute__((aligned(16))) uint8_t kt0[Tile<DK>::BYTES];  // selected rows, buffer 0
-  __shared__ __attribute__((aligned(16))) uint8_t kt1[Tile<DK>::BYTES];  // selected rows, buffer 1
+  __shared__ __attribute__((aligned(16))) uint8_t kt0[Tile<DK>::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t kt1[Tile<DK>::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t kt2[Tile<DK>::BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler
-                                                                 // keep wave-derived values in SGPRs
-  const int hg = wave & 3;          // head group
-  const int dh = wave >> 2;         // dimension half
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid & (kWave - 1);
+  const int g = lane >> 4;          // lane group: k-slots 8g .. 8g+7, output rows 4g .. 4g+3
+  const int h16 = lane & 15;        // head within the wave (MFMA column)
   const int c32 = lane & 31;
-  const int hf = lane >> 5;
   const int qi = blockIdx.x;
   const int sp = blockIdx.y;
-  const int head = hg * HPW + c32;
+  const int head = wave * HPW + h16;
   const bool head_ok = head < H;
-  const int kd0 = dh * (DK / 2);    // first key dim of this wave's logit half
-  const int vd0 = dh * (DV / 2);    // first value dim of this wave's output half
 
-  // last attendable position
   int t;
   if (PAGED) {
     t = qpos_or_ctx[qi] - 1;
@@ -214,13 +200,11 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     t = qpos_or_ctx[qi];
     if (t > n_kv - 1) t = n_kv - 1;
   }
-
   const int r0 = sp * rows_per_split;
   int r1 = r0 + rows_per_split;
   if (r1 > top_k) r1 = top_k;
   const int nrows = r1 > r0 ? r1 - r0 : 0;
 
-  // ---- translate the slice's selected positions to physical rows (invalid -> -1) ----
   for (int i = tid; i < nrows; i += NT) {
     const int s = idx[(size_t)qi * top_k + r0 + i];
     int row = -1;
@@ -235,16 +219,14 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     sh.rows[i] = row;
   }
 
-  // ---- queries of this wave's heads: B operand, k-step ks holds dims kd0 + 16ks + 8hf .. +8
-  // (k-steps >= QR are kept in LDS)
-  constexpr int QR = QSplit<DK>::QR;
+  // ---- queries: B operand of k-step ks = dims 32ks + 8g .. +8 of head `head` ----
   v8bf qf[QR];
   {
     const uint16_t* qrow = q + ((size_t)qi * H + (head_ok ? head : 0)) * DK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       v4i x = {0, 0, 0, 0};
-      if (head_ok) x = ld16(qrow + kd0 + 16 * ks + 8 * hf);
+      if (head_ok) x = ld16(qrow + 32 * ks + 8 * g);
       if (ks < QR)
         qf[ks < QR ? ks : 0] = as_v8bf(x);
       else
@@ -252,125 +234,108 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     }
   }
 
-  v16f o[NDB];
+  v4f o[NDB];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  for (int d = 0; d < NDB; ++d) o[d] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();   // per head (the 4 lanes of a head agree)
+  float l_run = 0.f;                 // this lane's part of the head's sum
 
   const int n_chunks = (nrows + CH - 1) / CH;
-  // physical row of entry c32 of chunk cc, or -1 (entries past the slice included)
   auto chunk_row = [&](int cc) -> int {
     const int e = cc * CH + c32;
     const int v = sh.rows[e < MAX_ROWS ? e : MAX_ROWS - 1];
     return e < nrows ? v : -1;
   };
-  __syncthreads();   // rows[] complete
-  int row_nx = chunk_row(0);                         // rows of the chunk gathered next
-  if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane, 0, Tile<DK>::GJ);
-  // bit k of vm_cur: key k of the current chunk is a valid selected row
-  u32 vm_cur = (u32)wave_ballot(row_nx >= 0);
+  constexpr int GW_HI = gather_count<DK>(0);   // loads per chunk of the first waves
+  const int my_loads = gather_count<DK>(wave);
+  __syncthreads();   // rows[] and the LDS queries complete
+  int row_nx = chunk_row(0);
+  if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane, 0, GJ);
+  u32 vm_a = (u32)wave_ballot(row_nx >= 0);   // validity of the chunk being computed
   row_nx = chunk_row(1);
-  __builtin_amdgcn_s_waitcnt(0);
+  if (n_chunks > 1) gather_chunk<DK>(kt1, kv, row_nx, wave, lane, 0, GJ);
+  u32 vm_b = (u32)wave_ballot(row_nx >= 0);   // validity of the next chunk
+  row_nx = chunk_row(2);                       // rows of the chunk gathered during step 0
+  // chunk 0 landed (chunk 1 may be in flight)
+  if (n_chunks > 1) {
+    if (my_loads == GW_HI) __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI - 1));
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   __syncthreads();
 
   // per-lane byte offsets inside a tile:
-  //  S^T A operand, k-step ks: key c32 (tile row tile_row(c32)), dims kd0 + 16ks + 8hf .. +8
-  //  ->  qk_off + 32 ks
-  const int qk_off = tile_row(c32) * RS + 2 * (kd0 + 8 * hf);
-  //  transposing read of the value product: input lane (m, q) of its 16-lane group points at
-  //  dims D + 4q of key 16k2 + 4hf + m (tile row 16k2 + hf + 4m; key + 8, the second half of
-  //  the k-slots, is tile row + 2), so output lane j holds dim D + j;
-  //  D = vd0 + 32d + 16 * (group parity)
+  //  logit product, key block kb, k-step ks: entry 16kb + h16, dims 32ks + 8g .. +8
+  //  ->  qk_off[kb] + 64 ks
+  const int qk_off0 = h16 * RS + 16 * g;
+  const int qk_off1 = (16 + h16) * RS + 16 * g;
+  //  value read, input lane (m, q) of group g: entry 4g + m (k-slots 8g .. 8g+3; entry
+  //  16 + 4g + m for k-slots 8g+4 .. 8g+7, 16 rows further), dims 16db + 4q
   const int tq = lane & 3, tm = (lane & 15) >> 2;
-  const int tr_off = tile_row(4 * hf + tm) * RS + 2 * (vd0 + 16 * ((lane >> 4) & 1) + 4 * tq);
-  static_assert(tile_row(8) - tile_row(0) == 2 && tile_row(12) - tile_row(4) == 2 &&
-                tile_row(16) - tile_row(0) == 16, "tile-row offsets of the value read");
+  const int tr_off = (4 * g + tm) * RS + 8 * tq;
 
-  auto step = [&](const lds_u8* tile, uint8_t* next_tile, int c) {
-    // the next chunk is gathered into the other buffer during this chunk's logit product
-    const bool more = c + 1 < n_chunks;
-    const u32 vm_nx = (u32)wave_ballot(row_nx >= 0);
-    const u32 vmask = vm_cur;
+  auto step = [&](const lds_u8* tile, uint8_t* gtile, int c) {
+    const bool more = c + 2 < n_chunks;    // chunk c+2 is gathered during this step
+    const u32 vmask = vm_a;
 
-    // ---- S^T = K Q^T for 32 keys x this wave's 32 heads, over its half of the dims ----
-    v16f sp_;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sp_[i] = 0.f;
-    const lds_u8* qk_base = tile + qk_off;
-    // LDS operands are fetched QPD k-steps ahead of their product
-    v4i ka[QPD];
-    v8bf kb[QPD];
+    // ---- S^T = K Q^T: 32 keys (two blocks of 16) x this wave's 16 heads ----
+    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    const lds_u8* b0 = tile + qk_off0;
+    const lds_u8* b1 = tile + qk_off1;
+    v4i ka[QPD], kb[QPD];
+    v8bf kq[QPD];
     auto fetch = [&](int k) {
-      ka[k % QPD] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(qk_base + 32 * k);
-      if (k >= QR) kb[k % QPD] = sh.qs[wave][k >= QR ? k - QR : 0][lane];
+      ka[k % QPD] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(b0 + 64 * k);
+      kb[k % QPD] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(b1 + 64 * k);
+      if (k >= QR) kq[k % QPD] = sh.qs[wave][k >= QR ? k - QR : 0][lane];
     };
 #pragma unroll
-    for (int ks = 0; ks < QPD; ++ks) fetch(ks);
+    for (int ks = 0; ks < QPD && ks < NKS; ++ks) fetch(ks);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const v4i av = ka[ks % QPD];
-      const v8bf b = ks < QR ? qf[ks < QR ? ks : 0] : kb[ks % QPD];
+      const v4i a0 = ka[ks % QPD], a1 = kb[ks % QPD];
+      const v8bf bq = ks < QR ? qf[ks < QR ? ks : 0] : kq[ks % QPD];
       if (ks + QPD < NKS) fetch(ks + QPD);
-      sp_ = mfma_bf16(as_v8bf(av), b, sp_);
-      // after product ks: this wave's wave-loads jj with gather_slot(jj) == ks
+      s0 = mfma16_bf16(as_v8bf(a0), bq, s0);
+      s1 = mfma16_bf16(as_v8bf(a1), bq, s1);
       const int j0 = first_load_at<NKS, GJ>(ks), j1 = first_load_at<NKS, GJ>(ks + 1);
-      if (j0 < j1 && more) gather_chunk<DK>(next_tile, kv, row_nx, wave, lane, j0, j1);
-      __builtin_amdgcn_sched_barrier(0);   // keep the fetch distance as written
+      if (j0 < j1 && more) gather_chunk<DK>(gtile, kv, row_nx, wave, lane, j0, j1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      sh.sx[wave][i4][lane] = v4f{sp_[4 * i4], sp_[4 * i4 + 1], sp_[4 * i4 + 2], sp_[4 * i4 + 3]};
-    lds_barrier();
 
-    // ---- online softmax (lane = head; element i is key 8(i/4) + 4hf + i%4) ----
-    // Lazy rescaling: the reference max m_run only moves when a logit exceeds it by more than
-    // 8 (log2 units), so probabilities stay below 2^8 and the accumulators are rarely
-    // rescaled.  The probabilities are first formed in one pass against the current m_run;
-    // only if some logit of the wave breaks the bound is the chunk redone in two passes with
-    // a new m_run.  Masked keys get a -inf bias (loads stay unconditional, no branches); a
-    // chunk whose keys are all valid skips the bias.
-    const u32 vml = vmask >> (4 * hf);   // bit 8a + b: key 8a + 4hf + b of the chunk
+    // ---- online softmax: lane holds keys 4g + i (s0) and 16 + 4g + i (s1) of head h16 ----
+    const u32 vml = vmask >> (4 * g);   // bit i: key 4g + i; bit 16 + i: key 16 + 4g + i
     float psum = 0.f;
-    v8bf pb[2];
+    v8bf pb;
     auto prob_pass = [&](float m_use, auto masked) {
       float mx = -__builtin_inff();
       psum = 0.f;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const v4f sa = sh.sx[hg][i4][lane], sb = sh.sx[hg + 4][i4][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          float nb = -m_use;
-          if constexpr (decltype(masked)::value)
-            nb = ((vml >> (8 * (i >> 2) + (i & 3))) & 1u) ? -m_use : -__builtin_inff();
-          const float y = fmaf(sa[e] + sb[e], scale_log2, nb);
-          mx = fmaxf(mx, y);
-          const float pv = __builtin_amdgcn_exp2f(y);
-          psum += pv;
-          pb[i >> 3][i & 7] = (__bf16)pv;
-        }
+      for (int i = 0; i < 8; ++i) {
+        const float x = i < 4 ? s0[i & 3] : s1[i & 3];
+        float nb = -m_use;
+        if constexpr (decltype(masked)::value)
+          nb = ((vml >> ((i < 4 ? 0 : 16) + (i & 3))) & 1u) ? -m_use : -__builtin_inff();
+        const float y = fmaf(x, scale_log2, nb);
+        mx = fmaxf(mx, y);
+        const float pv = __builtin_amdgcn_exp2f(y);
+        psum += pv;
+        pb[i] = (__bf16)pv;
       }
       return mx;
     };
-    // (with m_run = -inf every valid logit is +inf here, which forces the second path)
     const float over = vmask == 0xffffffffu ? prob_pass(m_run, std::false_type{})
                                             : prob_pass(m_run, std::true_type{});
     if (__ballot(!(over <= 8.f))) {
       float cmax = -__builtin_inff();
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const v4f sa = sh.sx[hg][i4][lane], sb = sh.sx[hg + 4][i4][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          const float bias = ((vml >> (8 * (i >> 2) + (i & 3))) & 1u) ? 0.f : -__builtin_inff();
-          cmax = fmaxf(cmax, fmaf(sa[e] + sb[e], scale_log2, bias));
-        }
+      for (int i = 0; i < 8; ++i) {
+        const float x = i < 4 ? s0[i & 3] : s1[i & 3];
+        const float bias = ((vml >> ((i < 4 ? 0 : 16) + (i & 3))) & 1u) ? 0.f : -__builtin_inff();
+        cmax = fmaxf(cmax, fmaf(x, scale_log2, bias));
       }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
       float alpha = 1.f;
       if (cmax > m_run + 8.f) {
@@ -381,68 +346,73 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       l_run *= alpha;
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+        for (int d = 0; d < NDB; ++d) o[d] *= alpha;
       }
     }
     l_run += psum;
 
-    // ---- O^T += V^T P^T; V^T slots j of half hf hold key 16k2 + 8(j/4) + 4hf + j%4 ----
+    // ---- O^T += V^T P^T over the 32 keys, 16 dims per block ----
     const lds_u8* tr_base = tile + tr_off;
+    constexpr int VPD = 4;
+    v4s fa[VPD], fb[VPD];
+    auto vfetch = [&](int d) {
+      fa[d % VPD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tr_base + 32 * d));
+      fb[d % VPD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tr_base + 16 * RS + 32 * d));
+    };
+#pragma unroll
+    for (int d = 0; d < VPD && d < NDB; ++d) vfetch(d);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const lds_u8* pa = tr_base + 16 * k2 * RS + 64 * d;
-        const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa));
-        const v4s vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(pa + 2 * RS));
-        v8bf a;
-        __builtin_memcpy(&a, &va, 8);
-        __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &vb, 8);
-        o[d] = mfma_bf16(a, pb[k2], o[d]);
-      }
+      v8bf a;
+      __builtin_memcpy(&a, &fa[d % VPD], 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &fb[d % VPD], 8);
+      if (d + VPD < NDB) vfetch(d + VPD);
+      o[d] = mfma16_bf16(a, pb, o[d]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    row_nx = chunk_row(c + 2);
-    vm_cur = vm_nx;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next chunk has landed
+    vm_a = vm_b;
+    vm_b = (u32)wave_ballot(row_nx >= 0);
+    row_nx = chunk_row(c + 3);
+    // chunk c+1 has landed: only this step's loads (chunk c+2) may still be in flight
+    if (more) {
+      if (my_loads == GW_HI) __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI));
+      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI - 1));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     __syncthreads();
   };
 
 #pragma unroll 1
-  for (int c = 0; c < n_chunks; c += 2) {
-    step((const lds_u8*)kt0, kt1, c);
+  for (int c = 0; c < n_chunks; c += 3) {
+    step((const lds_u8*)kt0, kt2, c);
     if (c + 1 < n_chunks) step((const lds_u8*)kt1, kt0, c + 1);
+    if (c + 2 < n_chunks) step((const lds_u8*)kt2, kt1, c + 2);
   }
 
-  // ---- epilogue: lane holds head `head`, dims vd0 + 32d + 8(i/4) + 4hf + i%4 ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- epilogue: lane holds head `head`, dims 16d + 4g + i ----
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
   if (!head_ok) return;
   if (n_split == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = out + ((size_t)qi * H + head) * DV;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 v;
-        v.x = pack_bf16x2(o[d][4 * j + 0] * inv, o[d][4 * j + 1] * inv);
-        v.y = pack_bf16x2(o[d][4 * j + 2] * inv, o[d][4 * j + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + vd0 + 32 * d + 8 * j + 4 * hf) = v;
-      }
+      uint2 v;
+      v.x = pack_bf16x2(o[d][0] * inv, o[d][1] * inv);
+      v.y = pack_bf16x2(o[d][2] * inv, o[d][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * d + 4 * g) = v;
     }
-    if (lse != nullptr && hf == 0 && dh == 0)
+    if (lse != nullptr && g == 0)
       lse[(size_t)qi * H + head] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
   } else {
     float* po = part_o + (((size_t)qi * n_split + sp) * H + head) * DV;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<v4f*>(po + vd0 + 32 * d + 8 * j + 4 * hf) =
-            v4f{o[d][4 * j + 0], o[d][4 * j + 1], o[d][4 * j + 2], o[d][4 * j + 3]};
-    if (hf == 0 && dh == 0) {
+    for (int d = 0; d < NDB; ++d) *reinterpret_cast<v4f*>(po + 16 * d + 4 * g) = o[d];
+    if (g == 0) {
       float* pm = part_ml + (((size_t)qi * n_split + sp) * H + head) * 2;
       pm[0] = m_run;
       pm[1] = l_tot;
