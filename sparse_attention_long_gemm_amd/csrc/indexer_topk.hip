@@ -26,11 +26,12 @@
 //   writes the sorted top_k positions.  No n_q x L score matrix is ever stored.
 //
 // Decode kernels (paged cache, one query per sequence)
-//   indexer_logits_paged: one wave scores 256 keys of one sequence; the A operand is the
-//   query's 64 heads (4 fragments of 16), the B operand 16 keys read through the page table,
-//   so the output lane owns one key and 4 heads; heads are summed in registers and across the
-//   4 lane groups.  Scores go to the workspace (4 bytes per key against 128 bytes of key read)
-//   and into a per-row histogram of their top 12 order-key bits.  The histogram locates the
+//   indexer_logits_paged: persistent waves, each streaming an equal share of all rows' keys
+//   (units of 32 positions) through the page table into its own LDS ring; the A operand is the
+//   query's 64 heads (4 fragments of 16), the B operand 16 keys from the ring, so the output
+//   lane owns one key and 4 heads; heads are summed in registers and across the 4 lane groups.
+//   Scores go to the workspace (4 bytes per key against 128 bytes of key read) and into a
+//   per-row histogram of their top 12 order-key bits.  The histogram locates the
 //   bin holding the top_k-th score; one pass over the scores, spread over many workgroups
 //   (dec_collect), lists every key above that bin and every key inside it; dec_finish picks
 //   the missing keys exactly among the latter and writes the row in position order.
