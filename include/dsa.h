@@ -129,7 +129,8 @@ dsa_status dsa_sparse_mqa_prefill(const uint16_t* q, const uint16_t* kv, int32_t
  * out      [B, H, D_v] bf16, lse [B, H] fp32 or NULL
  * The selected rows of each sequence are split over n_split workgroups (1 <= n_split <= 16,
  * top_k rows divided evenly; pass 0 for the library's choice) whose partial results are
- * merged by their log-sum-exp; the workspace holds the partials.
+ * merged by their log-sum-exp; the workspace holds the partials (each split's output
+ * normalised by its own softmax sum, in bf16, plus its running max and sum in fp32).
  * ------------------------------------------------------------------------------------- */
 size_t dsa_sparse_mqa_decode_workspace_size(int32_t B, int32_t H, int32_t D_v, int32_t top_k,
                                             int32_t n_split);

@@ -127,7 +127,8 @@ size_t dsa_sparse_mqa_decode_workspace_size(int32_t B, int32_t H, int32_t D_v, i
   int ns, rps;
   decode_split(B, top_k, n_split, &ns, &rps);
   if (ns == 1) return 0;
-  return (size_t)B * ns * H * ((size_t)D_v + 2) * sizeof(float);
+  // bf16 normalised partial outputs, then (max, sum) pairs in fp32
+  return (size_t)B * ns * H * ((size_t)D_v * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
@@ -156,8 +157,8 @@ dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
   a.n_q = B; a.H = H; a.D_k = D_k; a.D_v = D_v; a.top_k = top_k; a.scale = scale;
   a.n_split = ns; a.rows_per_split = rps; a.out = out; a.lse = lse;
   if (ns > 1) {
-    a.part_o = reinterpret_cast<float*>(workspace);
-    a.part_ml = a.part_o + (size_t)B * ns * H * D_v;
+    a.part_o = reinterpret_cast<uint16_t*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)B * ns * H * D_v);
   }
   return from_hip(dsa::launch_sparse_mqa(a, stream));
 }

@@ -34,8 +34,8 @@ struct MqaArgs {
   int n_split, rows_per_split;
   uint16_t* out;
   float* lse;
-  float* part_o;
-  float* part_ml;
+  uint16_t* part_o;   // decode partials: o / l in bf16 [n_q, n_split, H, D_v]
+  float* part_ml;     // running max (log2 units) and sum [n_q, n_split, H, 2]
 };
 bool mqa_shape_supported(int D_k, int D_v);
 hipError_t launch_sparse_mqa(const MqaArgs& a, hipStream_t stream);

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ qpos_or_ctx,
     const int32_t* __restrict__ page_table, int max_pages, int n_pages, int page_size, int n_kv,
     int H, int top_k, float scale_log2, int n_split, int rows_per_split,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml) {
   static_assert(DK % 32 == 0 && DV % 16 == 0 && DV <= DK, "shape");
   using Sh = MqaShared<DK>;
@@ -409,9 +409,16 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       lse[(size_t)qi * H + head] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
   } else {
-    float* po = part_o + (((size_t)qi * n_split + sp) * H + head) * DV;
+    // this split's output normalised by its own sum (bf16), merged by mqa_combine_kernel
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* po = part_o + (((size_t)qi * n_split + sp) * H + head) * DV;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) *reinterpret_cast<v4f*>(po + 16 * d + 4 * g) = o[d];
+    for (int d = 0; d < NDB; ++d) {
+      uint2 v;
+      v.x = pack_bf16x2(o[d][0] * inv, o[d][1] * inv);
+      v.y = pack_bf16x2(o[d][2] * inv, o[d][3] * inv);
+      *reinterpret_cast<uint2*>(po + 16 * d + 4 * g) = v;
+    }
     if (g == 0) {
       float* pm = part_ml + (((size_t)qi * n_split + sp) * H + head) * 2;
       pm[0] = m_run;
@@ -420,10 +427,11 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   }
 }
 
-// Merge the n_split partial results of one (query, head): weights exp2(m_i - M).
-// One workgroup per (query, head); each thread owns 4 consecutive dims.
+// Merge the n_split partial results of one (query, head): partial i holds o_i / l_i (bf16) with
+// its running max m_i and sum l_i, so o = sum_i w_i (o_i / l_i) / sum_i w_i with
+// w_i = exp2(m_i - M) l_i.  One workgroup per (query, head); each thread owns 4 consecutive dims.
 template <int DV>
-__global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const uint16_t* __restrict__ part_o,
                                                              const float* __restrict__ part_ml,
                                                              int H, int n_split,
                                                              uint16_t* __restrict__ out,
@@ -439,10 +447,13 @@ __global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const float* __rest
   if (M != -__builtin_inff()) {
     for (int i = 0; i < n_split; ++i) {
       const size_t b = base + (size_t)i * H;
-      const float wgt = exp2f(part_ml[b * 2] - M);
-      L += wgt * part_ml[b * 2 + 1];
-      const v4f v = *reinterpret_cast<const v4f*>(part_o + b * DV + d);
-      acc += wgt * v;
+      const float wgt = exp2f(part_ml[b * 2] - M) * part_ml[b * 2 + 1];
+      L += wgt;
+      const uint2 v = *reinterpret_cast<const uint2*>(part_o + b * DV + d);
+      acc[0] += wgt * bf16_to_f32((uint16_t)(v.x & 0xffffu));
+      acc[1] += wgt * bf16_to_f32((uint16_t)(v.x >> 16));
+      acc[2] += wgt * bf16_to_f32((uint16_t)(v.y & 0xffffu));
+      acc[3] += wgt * bf16_to_f32((uint16_t)(v.y >> 16));
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -59,7 +59,7 @@ def test_workspace_sizes():
     assert lib.dsa_indexer_topk_paged_workspace_size(64, 2048, 64) == \
         3 * 64 * rs * 4 + 64 * 4096 * 4 + 1024 + 64 * 2048 * 4
     # B=64, top_k=2048 -> 4 splits of 512 rows: partial o (fp32) + (max, sum) per head
-    assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 2048, 0) == 64 * 4 * 128 * 514 * 4
+    assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 2048, 0) == 64 * 4 * 128 * (512 * 2 + 8)
     assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 2048, 1) == 0
     assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 32, 0) == 0
 
