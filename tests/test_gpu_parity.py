@@ -13,11 +13,9 @@ import torch
 from gen import inputs as gi
 from oracle import dsa_oracle as orc
 
-pytestmark = pytest.mark.gpu
+from gates import ABS_TOL, LSE_REL, REL_TOL, check_attn, check_idx  # noqa: F401
 
-ABS_TOL = 1e-2
-REL_TOL = 1e-2
-LSE_REL = 1e-3
+pytestmark = pytest.mark.gpu
 
 
 def _dsa():
@@ -34,30 +32,6 @@ def to_dev(d):
     return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
 
-def check_idx(got, want, what=""):
-    got = got.cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got)
-    want = np.asarray(want)
-    assert got.shape == want.shape, what
-    bad = np.flatnonzero((got != want).any(axis=1))
-    assert bad.size == 0, f"{what}: {bad.size} index rows differ, first {bad[:5].tolist()}"
-
-
-def check_attn(o, lse, o_ref, lse_ref, what=""):
-    og = o.float().cpu().numpy()
-    err = np.abs(og - o_ref).max() if og.size else 0.0
-    ref_scale = np.abs(o_ref).max() if og.size else 0.0
-    assert err <= ABS_TOL, f"{what}: max abs err {err}"
-    if ref_scale > 0:
-        assert err / ref_scale <= REL_TOL, f"{what}: normalised err {err / ref_scale}"
-    if lse is not None:
-        lg = lse.cpu().numpy().astype(np.float64)
-        inf_ref = np.isneginf(lse_ref)
-        assert (np.isneginf(lg) == inf_ref).all(), f"{what}: -inf lse mismatch"
-        fin = ~inf_ref
-        if fin.any():
-            rel = np.abs(lg[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
-            assert rel.max() <= LSE_REL, f"{what}: lse rel err {rel.max()}"
-    return err
 
 
 def run_indexer(d, top_k=None):
