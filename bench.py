@@ -174,6 +174,41 @@ def copy_calibration(dev, nbytes=1 << 30, reps=3):
                                            "write_bytes": nbytes, "launches": reps}}), flush=True)
 
 
+def measured_ceilings(dsa, dev, reps: int = 3):
+    """What this GPU sustains: MFMA loops on register operands (the bf16 and FP8 instruction
+    shapes of the path) and a 4 GiB streaming read with 16-byte non-temporal loads; best of
+    `reps` launches each, timed with HIP events on the current stream."""
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_wg = 4 * n_cu
+    sink = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
+    out = {}
+    for kind, name in ((0, "bf16_mfma_tflops"), (1, "fp8_mfma_tflops")):
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = _ev(), _ev()
+            e0.record()
+            fl = dsa.ceiling_mfma(kind, n_wg, 20000, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[name] = best
+    src = torch.empty(1 << 30, dtype=torch.float32, device=dev)   # 4 GiB
+    src.fill_(1.0)
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = _ev(), _ev()
+        e0.record()
+        nb = dsa.ceiling_read(src, 2 * n_wg, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nb / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    out["hbm_read_gbps"] = best
+    del src
+    out["kernels"] = ("dsa_ceiling_mfma (32x32x16 bf16 / 16x16x128 FP8 chains, "
+                      f"{n_wg} workgroups x 8 waves) and dsa_ceiling_read (4 GiB, nt loads)")
+    return out
+
+
 def cpu_baseline(prefill: Prefill, budget_s: float = 20.0):
     """The fp64 oracle (as it stands) on a strided sample of the 128K prefill's rows, timed on
     this host; extrapolated to all rows by the exact per-row work model."""
@@ -317,6 +352,11 @@ def main():
         "decode": decode,
         "roofline": dominant,
     }
+    ceil = measured_ceilings(dsa, dev)
+    res["ceilings"] = ceil
+    roof_idx["frac_of_measured"] = roof_idx["achieved"] / ceil["fp8_mfma_tflops"]
+    roof_mqa["frac_of_measured"] = roof_mqa["achieved"] / ceil["bf16_mfma_tflops"]
+    decode["roofline"]["frac_of_measured"] = decode["roofline"]["achieved"] / ceil["hbm_read_gbps"]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_budget)

@@ -143,6 +143,25 @@ dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
                                  uint16_t* out, float* lse, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Measurement helpers (not part of the path).  They report what this GPU sustains on the
+ * instruction shapes and the memory stream the path uses, so that roofline fractions can be
+ * read against measured ceilings as well as against the published peaks.
+ *
+ * dsa_ceiling_mfma: n_wg workgroups of 512 threads each run `iters` iterations of independent
+ *   MFMA chains on register operands: kind 0 = v_mfma_f32_32x32x16_bf16 (bf16), kind 1 =
+ *   v_mfma_scale_f32_16x16x128_f8f6f4 with unscaled FP8 operands.  *flops (HOST pointer)
+ *   receives the flop count of the launch; sink: device float[n_wg * 512], overwritten.
+ * dsa_ceiling_read: streams `bytes` (a non-zero multiple of 16) from device memory `src` with
+ *   16-byte non-temporal loads over n_wg workgroups of 256 threads; sink: device
+ *   float[n_wg * 256], overwritten.
+ * Both return DSA_ERR_INVALID_ARG for out-of-range arguments (nothing launched).
+ * ------------------------------------------------------------------------------------- */
+dsa_status dsa_ceiling_mfma(int32_t kind, int32_t n_wg, int32_t iters, float* sink,
+                            double* flops, hipStream_t stream);
+dsa_status dsa_ceiling_read(const void* src, size_t bytes, int32_t n_wg, float* sink,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

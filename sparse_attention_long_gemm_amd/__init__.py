@@ -42,6 +42,8 @@ SIGNATURES = {
     "dsa_sparse_mqa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "dsa_sparse_mqa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                              _F, _I, _P, _P, _P, _Z, _P]),
+    "dsa_ceiling_mfma": (ctypes.c_int, [_I, _I, _I, _P, _P, _P]),
+    "dsa_ceiling_read": (ctypes.c_int, [_P, _Z, _I, _P, _P]),
 }
 
 _lib = None
@@ -245,3 +247,27 @@ __all__ = ["load_library", "DSAError", "indexer_topk", "indexer_topk_paged",
            "sparse_mqa_prefill", "sparse_mqa_decode", "indexer_topk_workspace_size",
            "indexer_topk_paged_workspace_size", "sparse_mqa_decode_workspace_size",
            "SIGNATURES", "LIB_PATH"]
+
+
+def ceiling_mfma(kind: int, n_wg: int, iters: int, sink: torch.Tensor) -> float:
+    """Launch the MFMA ceiling loop (kind 0: bf16 32x32x16, kind 1: FP8 16x16x128) on the
+    current stream; returns the launch's flop count.  sink: float32 [n_wg * 512] on the GPU."""
+    _need(sink, "sink", (torch.float32,), 1)
+    if sink.numel() < n_wg * 512:
+        raise ValueError("sink too small")
+    flops = ctypes.c_double(0.0)
+    _check(load_library().dsa_ceiling_mfma(kind, n_wg, iters, _ptr(sink), ctypes.byref(flops),
+                                           _stream(sink.device)), "dsa_ceiling_mfma")
+    return flops.value
+
+
+def ceiling_read(src: torch.Tensor, n_wg: int, sink: torch.Tensor) -> int:
+    """Launch the streaming-read ceiling kernel over src's bytes on the current stream;
+    returns the byte count.  sink: float32 [n_wg * 256] on the GPU."""
+    _need(sink, "sink", (torch.float32,), 1)
+    if sink.numel() < n_wg * 256 or not src.is_contiguous():
+        raise ValueError("sink too small or src not contiguous")
+    nbytes = src.numel() * src.element_size() // 16 * 16
+    _check(load_library().dsa_ceiling_read(_ptr(src), nbytes, n_wg, _ptr(sink),
+                                           _stream(sink.device)), "dsa_ceiling_read")
+    return nbytes

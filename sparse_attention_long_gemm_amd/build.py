@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["dsa_api.cpp", "indexer_topk.hip", "sparse_mqa.hip"]
+SOURCES = ["dsa_api.cpp", "indexer_topk.hip", "sparse_mqa.hip", "ceilings.hip"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU ops are switched off for all device code (see the design notes).

@@ -46,6 +46,18 @@ def test_abi_version_and_status_strings():
     assert lib.dsa_status_string(12345) == b"unknown dsa_status"
 
 
+def test_ceiling_helpers_reject_bad_arguments():
+    lib = dsa.load_library()
+    flops = ctypes.c_double(0.0)
+    fake = ctypes.c_void_p(16)   # never dereferenced: every call below fails its host checks
+    assert lib.dsa_ceiling_mfma(2, 1, 1, fake, ctypes.byref(flops), None) == -1
+    assert lib.dsa_ceiling_mfma(0, 0, 1, fake, ctypes.byref(flops), None) == -1
+    assert lib.dsa_ceiling_mfma(0, 1, 1, fake, None, None) == -1
+    assert lib.dsa_ceiling_read(fake, 24, 1, fake, None) == -1
+    assert lib.dsa_ceiling_read(fake, 0, 1, fake, None) == -1
+    assert lib.dsa_ceiling_read(None, 32, 1, fake, None) == -1
+
+
 def test_workspace_sizes():
     lib = dsa.load_library()
     # candidate lists of (score, position) pairs per row: room for top_k kept items plus two
