@@ -154,6 +154,8 @@ def test_prefill_tiny_full_path():
     (576, 512, 128, 300, 64, True),
     (576, 512, 128, 2100, 2048, True),
     (576, 512, 100, 500, 256, True),
+    (64, 64, 1, 100, 50, True),        # a single head: one wave active
+    (96, 64, 33, 150, 40, True),       # heads end inside a wave
 ])
 def test_mqa_shapes(D_k, D_v, H, L, top_k, sharp):
     wl = gi.Workload(name="m", L=L,
@@ -272,6 +274,21 @@ def test_decode_small(page_size, top_k, ctx, n_split, small_idx):
     i_ref, o_ref, l_ref = orc.decode(d)
     check_idx(idx, i_ref, "decode idx")
     check_attn(o, lse, o_ref, l_ref, "decode attn")
+
+
+@pytest.mark.parametrize("D_k,D_v,H", [(96, 64, 20), (64, 64, 128)])
+def test_decode_small_shapes(D_k, D_v, H):
+    sp = gi.DecodeSpec(B=3, page_size=64, idx=gi.IndexerSpec(top_k=128),
+                       mqa=gi.MqaSpec(H=H, D_k=D_k, D_v=D_v, sigma=1.0, scale=D_k ** -0.5),
+                       spare_pages=3, seed=5)
+    d = gi.decode_inputs(sp, ctx_lens=(700, 129, 2000))
+    step(f"decode shapes D_k={D_k} D_v={D_v} H={H}")
+    for n_split in (1, 2):
+        idx, o, lse = run_decode(d, n_split)
+        torch.cuda.synchronize()
+        i_ref, o_ref, l_ref = orc.decode(d)
+        check_idx(idx, i_ref, "decode idx")
+        check_attn(o, lse, o_ref, l_ref, f"decode attn split={n_split}")
 
 
 def test_decode_ties_large_candidate_list():
