@@ -54,12 +54,16 @@ constexpr int RPW = QB / NWAVE;  // query rows owned by each wave (filter + sele
 
 __device__ __forceinline__ v4i load16(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
 
-// 32 bytes [32g, 32g+32) of an FP8 row of d_I bytes (d_I a multiple of 16), zero past d_I.
+// The 32 bytes of an FP8 row of d_I bytes (d_I a multiple of 16) that lane group g feeds to a
+// 128-deep FP8 MFMA: 16-byte chunks g and g + 4, i.e. dims [16g, 16g+16) and [64+16g, 80+16g),
+// zero past d_I.  Any split of the 128 dims over lanes gives the same dot products as long as
+// both operands use it; this one lets a 16-key operand read from a 128-byte-row LDS tile hit
+// every bank once per pair of key rows.
 __device__ __forceinline__ v8i load_row32(const uint8_t* row, int g, int d_I, bool ok) {
   v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
   if (ok) {
-    if (32 * g < d_I) lo = load16(row + 32 * g);
-    if (32 * g + 16 < d_I) hi = load16(row + 32 * g + 16);
+    if (16 * g < d_I) lo = load16(row + 16 * g);
+    if (16 * g + 64 < d_I) hi = load16(row + 16 * g + 64);
   }
   v8i r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
@@ -213,7 +217,8 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(int lo, int hi) {
 }
 
 // Linear term sum_j w_j (q_j . k) = q_lin . k for one 16-key fragment and the 16 rows.
-// k-step ks of lane group g covers dims 32g + 8ks .. +8, like the FP8 fragments.
+// k-step ks of lane group g covers dims 16g + 8ks .. +8 (ks < 2) and 64 + 16g + 8(ks-2) .. +8,
+// the dims of the FP8 fragments.
 __device__ __forceinline__ v4f linear_term(const v8i& a, const PrefillShared& sh, int lane) {
   v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -229,8 +234,8 @@ __device__ __forceinline__ v4f linear_term(const v8i& a, const PrefillShared& sh
 
 // Key fragment (16 keys x 32 bytes per lane group) of tile row r0.. from the LDS key tile.
 __device__ __forceinline__ v8i frag_from_tile(const uint8_t* tile, int r, int g) {
-  const v4i lo = *reinterpret_cast<const v4i*>(tile + r * 128 + 16 * kchunk(r, 2 * g));
-  const v4i hi = *reinterpret_cast<const v4i*>(tile + r * 128 + 16 * kchunk(r, 2 * g + 1));
+  const v4i lo = *reinterpret_cast<const v4i*>(tile + r * 128 + 16 * kchunk(r, g));
+  const v4i hi = *reinterpret_cast<const v4i*>(tile + r * 128 + 16 * kchunk(r, g + 4));
   v8i a;
   a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
   a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   const int hg = wave & 3;       // head group: heads 16hg..16hg+15
   const int kh = wave >> 2;      // key-tile parity: tile 2i+kh of iteration i
   const int lane = tid & (kWave - 1);
-  const int g = lane >> 4;       // lane group: bytes [32g, 32g+32) of a row; output rows 4g..4g+3
+  const int g = lane >> 4;       // lane group: 16-byte chunks g, g+4 of a row; output rows 4g..4g+3
   const int c16 = lane & 15;     // output column = query row within the block
   const int q0 = blockIdx.x * QB;
   const bool heads_here = HPW * hg < H_I;
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int d = d0 + e;
-      const int gg = d >> 5, ks = (d & 31) >> 3, jj = d & 7;
+      const int gg = (d >> 4) & 3, ks = 2 * (d >> 6) + ((d >> 3) & 1), jj = d & 7;
       const int ln = 16 * gg + row;
       float v = acc[e];
 #pragma unroll
@@ -594,7 +599,7 @@ __device__ __forceinline__ v4i load16_nt(const uint8_t* p) {
 // row's global histogram (bins it touched only) when it moves to the next row, before a count
 // could overflow, and at its end.
 // Unit compute: the A operand is the row's query, 64 heads (4 fragments of 16 heads x 128
-// bytes, kept in registers), the B operand 16 keys (lane group g holds bytes [32g, 32g+32)
+// bytes, kept in registers), the B operand 16 keys (lane group g holds chunks g and g + 4
 // of key c16, read from the ring), so the output lane holds 4 heads of one key; heads are
 // summed in registers and across the 4 lane groups.  Keys whose page-table entry is outside
 // [0, n_pages) score as a zero key.  ALIGNED: the page size is a multiple of DEC_UNIT, so a
@@ -615,7 +620,7 @@ __global__ __launch_bounds__(SC_NT) void indexer_logits_paged_kernel(
   const int lane = tid & (kWave - 1);
   const int g = lane >> 4, c16 = lane & 15;
   u32* lh = lh_all[wave];
-  const bool lo_ok = 32 * g < d_I, hi_ok = 32 * g + 16 < d_I;
+  const bool lo_ok = 16 * g < d_I, hi_ok = 16 * g + 64 < d_I;
 
   // keys of row bb that are scored, and its unit count
   auto row_len = [&](int bb) { return min(max(ctx_lens[bb], 0), row_stride); };
@@ -773,10 +778,10 @@ __global__ __launch_bounds__(SC_NT) void indexer_logits_paged_kernel(
     bmax = -1;
   };
 
-  // lane's ring offsets of chunks 2g and 2g+1 of key c16 of fragment 0 (fragment f: + 2048 f)
+  // lane's ring offsets of chunks g and g+4 of key c16 of fragment 0 (fragment f: + 2048 f)
   static_assert(DEC_UNIT % 16 == 0 && DEC_UNIT <= 64, "unit size");
   const int hsw = (c16 >> 1) & 7;
-  const int rd0 = 128 * c16 + 16 * ((2 * g) ^ hsw), rd1 = 128 * c16 + 16 * ((2 * g + 1) ^ hsw);
+  const int rd0 = 128 * c16 + 16 * (g ^ hsw), rd1 = 128 * c16 + 16 * ((g + 4) ^ hsw);
   auto compute_unit = [&](const Cursor& c, int nb, bool page_ok) {
     const __attribute__((address_space(3))) uint8_t* rb =
         (const __attribute__((address_space(3))) uint8_t*)ring_all[wave][nb];
