@@ -350,7 +350,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     *reinterpret_cast<v4i*>(&sh.ktile[b][lr * 128 + 16 * kchunk(lr, lc + 1)]) = c1;
   };
 
-  const int n_iter = (t_max + BK2) / BK2;  // iterations covering keys 0..t_max
+  const int n_iter = (t_max + BK2) / BK2;  // key tiles covering keys 0..t_max
   {
     v4i c0, c1;
     load_tile(0, c0, c1);
@@ -358,37 +358,10 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   }
   __syncthreads();
 
-  // Iteration `it` computes the partial scores of keys [128 it, 128 it + 128) from key tile
-  // buffer it%2 while the next tile is fetched, then filters that iteration's keys.
-#pragma unroll 1
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-
-    // ---- cut candidate lists, all waves together (a cut stalls the whole workgroup at the
-    // next barrier, so cuts are batched): when any row ended the previous filter with less
-    // than one iteration of room, every row past half of its slack is cut ----
-    if (it >= 1) {
-      bool any_full = false;
-#pragma unroll
-      for (int v = 0; v < NWAVE; ++v) any_full |= sh.full[(it - 1) & 1][v] != 0;
-      if (any_full) {
-#pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-          const int q = q0 + RPW * wave + rr;
-          if (q >= n_q || it * BK2 > t_own[rr] || 2 * cnt[rr] <= top_k + cap) continue;
-          int kept;
-          thr[rr] = wave_cut(cand_score + (size_t)q * cap, cand_pos + (size_t)q * cap, cnt[rr],
-                             top_k, cap, wave_max_u32(hi_seen[rr]), rowh[rr],
-                             sh.rhist[RPW * wave + rr], sh.hist[wave], &kept);
-          cnt[rr] = kept;
-        }
-      }
-    }
-
-    // ---- fetch the next key tile into registers (stored to LDS after the MFMA work) ----
-    v4i nc0 = {0, 0, 0, 0}, nc1 = {0, 0, 0, 0};
-    if (it + 1 < n_iter) load_tile(it + 1, nc0, nc1);
-
+  // Scores of key tile `kt` (keys [128 kt, 128 kt + 128)) from key buffer kt%2 into partial
+  // buffer kt%2, then the next tile (already in registers) into the other key buffer.
+  auto compute = [&](int kt, const v4i& nc0, const v4i& nc1) {
+    const int buf = kt & 1;
     const uint8_t* tile = sh.ktile[buf] + kh * BK * 128;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -411,11 +384,14 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       if (f == hg)
         *reinterpret_cast<v4f*>(&sh.plin[buf][kh][c16][16 * f + 4 * g]) = linear_term(a, sh, lane);
     }
-    if (it + 1 < n_iter) store_tile(buf ^ 1, nc0, nc1);
-    __syncthreads();
+    if (kt + 1 < n_iter) store_tile(buf ^ 1, nc0, nc1);
+  };
 
-    // ---- this wave's rows: I = (sum_j w_j x_j + sum_j w_j |x_j|) / 2 = sum_j w_j ReLU(x_j);
-    // causal mask, threshold filter, ordered append.  All LDS reads are issued first. ----
+  // This wave's rows over key tile `kt`: I = (sum_j w_j x_j + sum_j w_j |x_j|) / 2 =
+  // sum_j w_j ReLU(x_j); causal mask, threshold filter, ordered append.  All LDS reads are
+  // issued first.  Rows that could overflow in the next filter are flagged in full[kt % 2].
+  auto filter = [&](int kt) {
+    const int buf = kt & 1;
     float scv[RPW][2];
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
@@ -432,10 +408,10 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       const int r = RPW * wave + rr;
       const int q = q0 + r;
       const int t = t_own[rr];
-      if (q >= n_q || it * BK2 > t) continue;
+      if (q >= n_q || kt * BK2 > t) continue;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int s = it * BK2 + half * BK + lane;
+        const int s = kt * BK2 + half * BK + lane;
         const float sc = scv[rr][half];
         const bool pass = (s <= t) && (sc > thr[rr]);
         const uint64_t m = wave_ballot(pass);
@@ -452,12 +428,55 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
         }
       }
     }
-    // flag rows that could overflow in the next filter; they are cut after the next barrier
     bool full = false;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr)
-      full |= (q0 + RPW * wave + rr < n_q) && cnt[rr] + BK2 > cap && (it + 1) * BK2 <= t_own[rr];
-    if (lane == 0) sh.full[it & 1][wave] = full ? 1 : 0;
+      full |= (q0 + RPW * wave + rr < n_q) && cnt[rr] + BK2 > cap && (kt + 1) * BK2 <= t_own[rr];
+    if (lane == 0) sh.full[buf][wave] = full ? 1 : 0;
+  };
+
+  // Step `it` scores key tile it and filters key tile it-1 (scored in the previous step), then
+  // synchronizes.  The two waves that share a SIMD (waves w and w+4, opposite tile parities)
+  // take the two phases in opposite orders, so one wave's VALU-heavy filter runs beside the
+  // other wave's MFMA work.
+#pragma unroll 1
+  for (int it = 0; it <= n_iter; ++it) {
+    const int kf = it - 1;   // tile filtered in this step
+
+    // ---- cut candidate lists, all waves together (a cut stalls the whole workgroup at the
+    // next barrier, so cuts are batched): when any row ended the previous filter with less
+    // than one tile of room, every row past half of its slack is cut ----
+    if (kf >= 1) {
+      bool any_full = false;
+#pragma unroll
+      for (int v = 0; v < NWAVE; ++v) any_full |= sh.full[(kf - 1) & 1][v] != 0;
+      if (any_full) {
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+          const int q = q0 + RPW * wave + rr;
+          if (q >= n_q || kf * BK2 > t_own[rr] || 2 * cnt[rr] <= top_k + cap) continue;
+          int kept;
+          thr[rr] = wave_cut(cand_score + (size_t)q * cap, cand_pos + (size_t)q * cap, cnt[rr],
+                             top_k, cap, wave_max_u32(hi_seen[rr]), rowh[rr],
+                             sh.rhist[RPW * wave + rr], sh.hist[wave], &kept);
+          cnt[rr] = kept;
+        }
+      }
+    }
+
+    // ---- fetch the next key tile into registers (stored to LDS after the MFMA work) ----
+    v4i nc0 = {0, 0, 0, 0}, nc1 = {0, 0, 0, 0};
+    if (it + 1 < n_iter) load_tile(it + 1, nc0, nc1);
+
+#pragma unroll 1
+    for (int ph = 0; ph < 2; ++ph) {
+      if (ph == kh) {
+        if (it < n_iter) compute(it, nc0, nc1);
+      } else {
+        if (kf >= 0) filter(kf);
+      }
+    }
+    __syncthreads();
   }
 
   // ---- final exact selection of this wave's rows ----
