@@ -100,49 +100,72 @@ struct MqaShared {
   int rows[MAX_ROWS];   // physical row of each selected entry, or -1
 };
 
-// Issue wave-loads jj0 <= jj < jj1 (compile-time constants once the caller's loop is unrolled)
-// of this wave's part of one chunk's gather into `tile`: wave-load j = wave + NW jj covers 64
-// consecutive 16-byte tile slots, lane i filling slot 64j + i.  `row` holds, in lane l (and
-// l + 32), the physical row of entry l of the chunk or -1; each lane takes its slot's row from
-// there.  Pad slots, slots past the tile and entries that are not valid rows get a harmless
-// load of the first 16 bytes of the KV array (pad slots are never read; invalid keys are
-// masked out of the softmax).  The load is written out (global_load_lds_dwordx4: 16 bytes
-// per lane into LDS at M0 + 16 * lane) so that the compiler does not count it as an
-// outstanding LDS access, which would make it wait for all LDS traffic wherever a tile read
-// is consumed; its waits are the explicit ones at the end of each chunk.
+// Byte offset, inside its KV row, of the 16-byte slot that this lane fills in wave-load jj of
+// its wave's part of a chunk's gather (wave-load j = wave + NW jj covers 64 consecutive tile
+// slots, lane i filling slot 64j + i), or -1 for a pad slot or a slot past the tile.  These
+// depend only on the wave and lane, so they are computed once per workgroup.
 template <int DK>
+__device__ __forceinline__ void gather_plan(int wave, int lane, int (&slot_off)[Tile<DK>::GJ]) {
+  using T = Tile<DK>;
+#pragma unroll
+  for (int jj = 0; jj < T::GJ; ++jj) {
+    const int u = (wave + NW * jj) * kWave + lane;
+    const int r = u / T::SLOTS;
+    const int p = u - r * T::SLOTS;
+    slot_off[jj] = (r < CH && p < T::NCH) ? 16 * p : -1;
+  }
+}
+
+// Issue wave-loads jj0 <= jj < jj1 (compile-time constants once the caller's loop is unrolled)
+// of this wave's part of one chunk's gather into `tile`.  `row` holds, in lane l (and l + 32),
+// the physical row of entry l of the chunk or -1; each lane takes its slot's row from there.
+// Slots that are pads, lie past the tile or belong to entries that are not valid rows get a
+// harmless load of the first 16 bytes of the KV array (pad slots are never read; invalid keys
+// are masked out of the softmax).  OFF32: the KV array is under 2 GiB, so the address is the
+// array base (scalar) plus a 32-bit per-lane offset.  The load is written out
+// (global_load_lds_dwordx4: 16 bytes per lane into LDS at M0 + 16 * lane) so that the compiler
+// does not count it as an outstanding LDS access, which would make it wait for all LDS traffic
+// wherever a tile read is consumed; its waits are the explicit ones at the end of each chunk.
+template <int DK, bool OFF32>
 __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __restrict__ kv,
-                                             int row, int wave, int lane, int jj0, int jj1) {
+                                             int row, int wave, int lane, int jj0, int jj1,
+                                             const int (&slot_off)[Tile<DK>::GJ]) {
   using T = Tile<DK>;
   constexpr int GJ = T::GJ;
-  int ln;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
 #pragma unroll
   for (int jj = 0; jj < GJ; ++jj) {
     if (jj < jj0 || jj >= jj1) continue;
     const int j = wave + NW * jj;
     if (GJ * NW > T::LOADS && j >= T::LOADS) break;     // wave-uniform
-    const int u = j * kWave + ln;
-    const int r = u / T::SLOTS;
-    const int p = u - r * T::SLOTS;
     int rw;
     if constexpr (T::SLOTS >= kWave) {
+      // the 64 slots span rows rlo and rlo + 1; lanes from `cut` on are in the second
       const int rlo = (j * kWave) / T::SLOTS;
+      const int cut = (rlo + 1) * T::SLOTS - j * kWave;
       const int ra = __builtin_amdgcn_readlane(row, rlo < CH ? rlo : CH - 1);
       const int rb = __builtin_amdgcn_readlane(row, rlo + 1 < CH ? rlo + 1 : CH - 1);
-      rw = r == rlo ? ra : rb;
+      rw = lane >= cut ? rb : ra;
     } else {
-      rw = __shfl(row, r & (CH - 1));
+      rw = __shfl(row, ((j * kWave + lane) / T::SLOTS) & (CH - 1));
     }
-    const bool real = (r < CH) & (rw >= 0) & (p < T::NCH);
-    const size_t off = (size_t)(u32)(real ? rw : 0) * DK + (u32)(real ? 8 * p : 0);
+    const int so = slot_off[jj];
+    const bool real = (rw >= 0) & (so >= 0);
     const u32 lds = (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(tile + 16 * kWave * j);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(kv + off), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory", "m0");
+    if constexpr (OFF32) {
+      const u32 off = real ? __umul24((u32)rw, 2 * DK) + (u32)so : 0u;
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                   :
+                   : "v"(off), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(kv)
+                   : "memory", "m0");
+    } else {
+      const size_t off = real ? (size_t)(u32)rw * DK + (u32)(so >> 1) : 0;
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(kv + off), "s"(__builtin_amdgcn_readfirstlane(lds))
+                   : "memory", "m0");
+    }
 #pragma clang diagnostic pop
   }
 }
@@ -161,7 +184,7 @@ __host__ __device__ constexpr int vm_wait_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-template <int DK, int DV, bool PAGED>
+template <int DK, int DV, bool PAGED, bool OFF32>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ qpos_or_ctx,
@@ -248,12 +271,14 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   };
   constexpr int GW_HI = gather_count<DK>(0);   // loads per chunk of the first waves
   const int my_loads = gather_count<DK>(wave);
+  int slot_off[GJ];
+  gather_plan<DK>(wave, lane, slot_off);
   __syncthreads();   // rows[] and the LDS queries complete
   int row_nx = chunk_row(0);
-  if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane, 0, GJ);
+  if (n_chunks > 0) gather_chunk<DK, OFF32>(kt0, kv, row_nx, wave, lane, 0, GJ, slot_off);
   u32 vm_a = (u32)wave_ballot(row_nx >= 0);   // validity of the chunk being computed
   row_nx = chunk_row(1);
-  if (n_chunks > 1) gather_chunk<DK>(kt1, kv, row_nx, wave, lane, 0, GJ);
+  if (n_chunks > 1) gather_chunk<DK, OFF32>(kt1, kv, row_nx, wave, lane, 0, GJ, slot_off);
   u32 vm_b = (u32)wave_ballot(row_nx >= 0);   // validity of the next chunk
   row_nx = chunk_row(2);                       // rows of the chunk gathered during step 0
   // chunk 0 landed (chunk 1 may be in flight)
@@ -300,7 +325,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       s0 = mfma16_bf16(as_v8bf(a0), bq, s0);
       s1 = mfma16_bf16(as_v8bf(a1), bq, s1);
       const int j0 = first_load_at<NKS, GJ>(ks), j1 = first_load_at<NKS, GJ>(ks + 1);
-      if (j0 < j1 && more) gather_chunk<DK>(gtile, kv, row_nx, wave, lane, j0, j1);
+      if (j0 < j1 && more) gather_chunk<DK, OFF32>(gtile, kv, row_nx, wave, lane, j0, j1, slot_off);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -468,14 +493,20 @@ __global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const uint16_t* __r
 template <int DK, int DV>
 hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
+  // rows of the KV array, and whether its bytes fit a 31-bit offset
+  const long long kv_rows =
+      a.page_table == nullptr ? (long long)a.n_kv : (long long)a.n_pages * a.page_size;
+  const bool off32 = kv_rows * DK * 2 < (1ll << 31);
   if (a.page_table == nullptr) {
-    hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false>), dim3(a.n_q, 1), dim3(NT), 0, stream,
+    auto kern = off32 ? sparse_mqa_kernel<DK, DV, false, true> : sparse_mqa_kernel<DK, DV, false, false>;
+    hipLaunchKernelGGL(kern, dim3(a.n_q, 1), dim3(NT), 0, stream,
                        a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, 0, 0, 1, a.n_kv, a.H, a.top_k,
                        scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr);
     return hipGetLastError();
   }
   const int rps = a.rows_per_split;
-  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true>), dim3(a.n_q, a.n_split), dim3(NT), 0,
+  auto kern = off32 ? sparse_mqa_kernel<DK, DV, true, true> : sparse_mqa_kernel<DK, DV, true, false>;
+  hipLaunchKernelGGL(kern, dim3(a.n_q, a.n_split), dim3(NT), 0,
                      stream, a.q, a.kv, a.idx, a.qpos_or_ctx, a.page_table, a.max_pages,
                      a.n_pages, a.page_size, 0, a.H, a.top_k, scale_log2, a.n_split, rps, a.out,
                      a.lse, a.part_o, a.part_ml);

@@ -193,6 +193,38 @@ def test_mqa_skips_invalid_entries_and_empty_rows():
     assert (o[80] == 0).all() and torch.isneginf(lse[80]).all()
 
 
+def test_mqa_kv_array_over_2gib():
+    """A KV array larger than 2 GiB (rows addressed with 64-bit offsets), rows selected on both
+    sides of the 2 GiB mark."""
+    dsa = _dsa()
+    n_kv, H, D_k, D_v, top_k, n_q = 1_900_000, 128, 576, 512, 96, 3
+    g = torch.Generator().manual_seed(21)
+    hi0 = (1 << 31) // (2 * D_k) + 1           # first row wholly past 2 GiB
+    idx = torch.empty((n_q, top_k), dtype=torch.int32)
+    for i in range(n_q):
+        lo = torch.randperm(hi0, generator=g)[: top_k // 2]
+        hi = hi0 + torch.randperm(n_kv - hi0, generator=g)[: top_k - top_k // 2]
+        idx[i] = torch.cat([lo, hi]).to(torch.int32)
+    rows = torch.unique(idx.flatten().long())
+    vals = torch.randn((rows.numel(), D_k), generator=g).to(torch.bfloat16)
+    q = (torch.randn((n_q, H, D_k), generator=g) * 0.3).to(torch.bfloat16)
+    step(f"mqa kv over 2 GiB: n_kv={n_kv} rows, D_k={D_k}, k={top_k}")
+    kv = torch.zeros((n_kv, D_k), dtype=torch.bfloat16, device="cuda")
+    kv[rows.cuda()] = vals.cuda()
+    q_pos = torch.full((n_q,), n_kv - 1, dtype=torch.int32)
+    scale = D_k ** -0.5
+    o, lse = dsa.sparse_mqa_prefill(q.cuda(), kv, idx.cuda(), q_pos.cuda(), D_v, scale)
+    torch.cuda.synchronize()
+    pos = {int(r): k for k, r in enumerate(rows.tolist())}
+    o_ref = np.zeros((n_q, H, D_v))
+    l_ref = np.zeros((n_q, H))
+    for i in range(n_q):
+        sel = vals[[pos[int(r)] for r in idx[i].tolist()]].double().numpy()
+        o_ref[i], l_ref[i] = orc.sparse_mqa(q[i].double().numpy(), sel, D_v, scale)
+    check_attn(o, lse, o_ref, l_ref, "kv > 2 GiB")
+    del kv
+
+
 def test_prefill_L32768_sampled():
     """Full DSA prefill at L=32768 (indexer on all rows, then MQA), sampled rows."""
     wl = gi.prefill_workload(32768)
