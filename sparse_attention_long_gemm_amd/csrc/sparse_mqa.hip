@@ -122,7 +122,8 @@ __device__ __forceinline__ void gather_plan(int wave, int lane, int (&slot_off)[
 // Slots that are pads, lie past the tile or belong to entries that are not valid rows get a
 // harmless load of the first 16 bytes of the KV array (pad slots are never read; invalid keys
 // are masked out of the softmax).  OFF32: the KV array is under 2 GiB, so the address is the
-// array base (scalar) plus a 32-bit per-lane offset.  The load is written out
+// array base (scalar) plus a 32-bit per-lane offset; otherwise each of the two rows that a
+// wave-load of a long row touches gets its own 64-bit scalar base.  The load is written out
 // (global_load_lds_dwordx4: 16 bytes per lane into LDS at M0 + 16 * lane) so that the compiler
 // does not count it as an outstanding LDS access, which would make it wait for all LDS traffic
 // wherever a tile read is consumed; its waits are the explicit ones at the end of each chunk.
@@ -137,33 +138,52 @@ __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __re
     if (jj < jj0 || jj >= jj1) continue;
     const int j = wave + NW * jj;
     if (GJ * NW > T::LOADS && j >= T::LOADS) break;     // wave-uniform
-    int rw;
+    const int so = slot_off[jj];
+    const u32 lds = __builtin_amdgcn_readfirstlane(
+        (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(tile + 16 * kWave * j));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
     if constexpr (T::SLOTS >= kWave) {
-      // the 64 slots span rows rlo and rlo + 1; lanes from `cut` on are in the second
+      // the 64 slots span rows rlo and rlo + 1 (row numbers ra, rb: scalar); lanes from `cut`
+      // on are in the second
       const int rlo = (j * kWave) / T::SLOTS;
       const int cut = (rlo + 1) * T::SLOTS - j * kWave;
       const int ra = __builtin_amdgcn_readlane(row, rlo < CH ? rlo : CH - 1);
       const int rb = __builtin_amdgcn_readlane(row, rlo + 1 < CH ? rlo + 1 : CH - 1);
-      rw = lane >= cut ? rb : ra;
+      const bool second = lane >= cut;
+      const int rw = second ? rb : ra;
+      const bool real = (rw >= 0) & (so >= 0);
+      if constexpr (OFF32) {
+        const u32 off = real ? __umul24((u32)rw, 2 * DK) + (u32)so : 0u;
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                     :
+                     : "v"(off), "s"(lds), "s"(kv)
+                     : "memory", "m0");
+      } else {
+        // any array size: each of the two rows gets a 64-bit scalar base and the lanes of
+        // each row load in their own (exec-masked) instruction with a small offset
+        const uint16_t* base_a = kv + (size_t)(u32)(ra >= 0 ? ra : 0) * DK;
+        const uint16_t* base_b = kv + (size_t)(u32)(rb >= 0 ? rb : 0) * DK;
+        const u32 off = real ? (u32)so : 0u;
+        if (!second)
+          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                       :
+                       : "v"(off), "s"(lds), "s"(base_a)
+                       : "memory", "m0");
+        else
+          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                       :
+                       : "v"(off), "s"(lds), "s"(base_b)
+                       : "memory", "m0");
+      }
     } else {
-      rw = __shfl(row, ((j * kWave + lane) / T::SLOTS) & (CH - 1));
-    }
-    const int so = slot_off[jj];
-    const bool real = (rw >= 0) & (so >= 0);
-    const u32 lds = (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(tile + 16 * kWave * j);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-    if constexpr (OFF32) {
-      const u32 off = real ? __umul24((u32)rw, 2 * DK) + (u32)so : 0u;
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-                   :
-                   : "v"(off), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(kv)
-                   : "memory", "m0");
-    } else {
+      // small rows: several rows per wave-load, per-lane 64-bit addresses
+      const int rw = __shfl(row, ((j * kWave + lane) / T::SLOTS) & (CH - 1));
+      const bool real = (rw >= 0) & (so >= 0);
       const size_t off = real ? (size_t)(u32)rw * DK + (u32)(so >> 1) : 0;
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                    :
-                   : "v"(kv + off), "s"(__builtin_amdgcn_readfirstlane(lds))
+                   : "v"(kv + off), "s"(lds)
                    : "memory", "m0");
     }
 #pragma clang diagnostic pop
