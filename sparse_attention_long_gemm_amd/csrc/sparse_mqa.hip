@@ -102,8 +102,9 @@ struct MqaShared {
 
 // Byte offset, inside its KV row, of the 16-byte slot that this lane fills in wave-load jj of
 // its wave's part of a chunk's gather (wave-load j = wave + NW jj covers 64 consecutive tile
-// slots, lane i filling slot 64j + i), or -1 for a pad slot or a slot past the tile.  These
-// depend only on the wave and lane, so they are computed once per workgroup.
+// slots, lane i filling slot 64j + i), or 0 for a pad slot or a slot past the tile (those
+// load the start of a row and are never read).  These depend only on the wave and lane, so
+// they are computed once per workgroup.
 template <int DK>
 __device__ __forceinline__ void gather_plan(int wave, int lane, int (&slot_off)[Tile<DK>::GJ]) {
   using T = Tile<DK>;
@@ -112,22 +113,19 @@ __device__ __forceinline__ void gather_plan(int wave, int lane, int (&slot_off)[
     const int u = (wave + NW * jj) * kWave + lane;
     const int r = u / T::SLOTS;
     const int p = u - r * T::SLOTS;
-    slot_off[jj] = (r < CH && p < T::NCH) ? 16 * p : -1;
+    slot_off[jj] = (r < CH && p < T::NCH) ? 16 * p : 0;
   }
 }
 
 // Issue wave-loads jj0 <= jj < jj1 (compile-time constants once the caller's loop is unrolled)
 // of this wave's part of one chunk's gather into `tile`.  `row` holds, in lane l (and l + 32),
 // the physical row of entry l of the chunk or -1; each lane takes its slot's row from there.
-// Slots that are pads, lie past the tile or belong to entries that are not valid rows get a
-// harmless load of the first 16 bytes of the KV array (pad slots are never read; invalid keys
-// are masked out of the softmax).  OFF32: the KV array is under 2 GiB, so the address is the
-// array base (scalar) plus a 32-bit per-lane offset; otherwise each of the two rows that a
-// wave-load of a long row touches gets its own 64-bit scalar base.  The load is written out
+// Entries that are not valid rows load row 0 (their keys are masked out of the softmax).  The
+// load is written out
 // (global_load_lds_dwordx4: 16 bytes per lane into LDS at M0 + 16 * lane) so that the compiler
 // does not count it as an outstanding LDS access, which would make it wait for all LDS traffic
 // wherever a tile read is consumed; its waits are the explicit ones at the end of each chunk.
-template <int DK, bool OFF32>
+template <int DK>
 __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __restrict__ kv,
                                              int row, int wave, int lane, int jj0, int jj1,
                                              const int (&slot_off)[Tile<DK>::GJ]) {
@@ -144,43 +142,34 @@ __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __re
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
     if constexpr (T::SLOTS >= kWave) {
-      // the 64 slots span rows rlo and rlo + 1 (row numbers ra, rb: scalar); lanes from `cut`
-      // on are in the second
+      // The 64 slots span rows rlo and rlo + 1 of the tile; lanes below `cut` fill the first.
+      // Each row gets a 64-bit scalar base (row 0 for an entry that is not a valid row), and
+      // the two lane ranges load in two instructions under scalar exec masks, so the address
+      // work is scalar; a pad slot or a slot past the tile loads the start of its row.
       const int rlo = (j * kWave) / T::SLOTS;
       const int cut = (rlo + 1) * T::SLOTS - j * kWave;
       const int ra = __builtin_amdgcn_readlane(row, rlo < CH ? rlo : CH - 1);
       const int rb = __builtin_amdgcn_readlane(row, rlo + 1 < CH ? rlo + 1 : CH - 1);
-      const bool second = lane >= cut;
-      const int rw = second ? rb : ra;
-      const bool real = (rw >= 0) & (so >= 0);
-      if constexpr (OFF32) {
-        const u32 off = real ? __umul24((u32)rw, 2 * DK) + (u32)so : 0u;
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-                     :
-                     : "v"(off), "s"(lds), "s"(kv)
-                     : "memory", "m0");
-      } else {
-        // any array size: each of the two rows gets a 64-bit scalar base and the lanes of
-        // each row load in their own (exec-masked) instruction with a small offset
-        const uint16_t* base_a = kv + (size_t)(u32)(ra >= 0 ? ra : 0) * DK;
-        const uint16_t* base_b = kv + (size_t)(u32)(rb >= 0 ? rb : 0) * DK;
-        const u32 off = real ? (u32)so : 0u;
-        if (!second)
-          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-                       :
-                       : "v"(off), "s"(lds), "s"(base_a)
-                       : "memory", "m0");
-        else
-          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-                       :
-                       : "v"(off), "s"(lds), "s"(base_b)
-                       : "memory", "m0");
-      }
+      const uint16_t* base_a = kv + (size_t)(u32)(ra >= 0 ? ra : 0) * DK;
+      const uint16_t* base_b = kv + (size_t)(u32)(rb >= 0 ? rb : 0) * DK;
+      const uint64_t mask_a = cut >= kWave ? ~0ull : ((1ull << cut) - 1ull);
+      uint64_t saved;
+      asm volatile(
+          "s_mov_b64 %[sv], exec\n\t"
+          "s_and_b64 exec, %[sv], %[ma]\n\t"
+          "s_mov_b32 m0, %[lds]\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %[off], %[ba]\n\t"
+          "s_andn2_b64 exec, %[sv], %[ma]\n\t"
+          "global_load_lds_dwordx4 %[off], %[bb]\n\t"
+          "s_mov_b64 exec, %[sv]"
+          : [sv] "=&s"(saved)
+          : [ma] "s"(mask_a), [lds] "s"(lds), [off] "v"(so), [ba] "s"(base_a), [bb] "s"(base_b)
+          : "memory", "m0");
     } else {
-      // small rows: several rows per wave-load, per-lane 64-bit addresses
+      // short rows: several rows per wave-load, per-lane 64-bit addresses
       const int rw = __shfl(row, ((j * kWave + lane) / T::SLOTS) & (CH - 1));
-      const bool real = (rw >= 0) & (so >= 0);
-      const size_t off = real ? (size_t)(u32)rw * DK + (u32)(so >> 1) : 0;
+      const size_t off = rw >= 0 ? (size_t)(u32)rw * DK + (u32)(so >> 1) : 0;
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                    :
                    : "v"(kv + off), "s"(lds)
@@ -189,6 +178,10 @@ __device__ __forceinline__ void gather_chunk(uint8_t* tile, const uint16_t* __re
 #pragma clang diagnostic pop
   }
 }
+
+// Load instructions per wave-load (two when a wave-load spans two rows of long rows).
+template <int DK>
+__device__ constexpr int gather_insts() { return Tile<DK>::SLOTS >= kWave ? 2 : 1; }
 
 // Number of wave-loads of one chunk's gather that wave `wave` issues.
 template <int DK>
@@ -204,7 +197,7 @@ __host__ __device__ constexpr int vm_wait_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-template <int DK, int DV, bool PAGED, bool OFF32>
+template <int DK, int DV, bool PAGED>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ qpos_or_ctx,
@@ -289,22 +282,24 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const int v = sh.rows[e < MAX_ROWS ? e : MAX_ROWS - 1];
     return e < nrows ? v : -1;
   };
-  constexpr int GW_HI = gather_count<DK>(0);   // loads per chunk of the first waves
-  const int my_loads = gather_count<DK>(wave);
+  // load instructions per chunk of the first waves, and of this wave
+  constexpr int GW_HI = gather_count<DK>(0) * gather_insts<DK>();
+  constexpr int GW_STEP = gather_insts<DK>();   // the other waves issue one wave-load fewer
+  const int my_loads = gather_count<DK>(wave) * gather_insts<DK>();
   int slot_off[GJ];
   gather_plan<DK>(wave, lane, slot_off);
   __syncthreads();   // rows[] and the LDS queries complete
   int row_nx = chunk_row(0);
-  if (n_chunks > 0) gather_chunk<DK, OFF32>(kt0, kv, row_nx, wave, lane, 0, GJ, slot_off);
+  if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane, 0, GJ, slot_off);
   u32 vm_a = (u32)wave_ballot(row_nx >= 0);   // validity of the chunk being computed
   row_nx = chunk_row(1);
-  if (n_chunks > 1) gather_chunk<DK, OFF32>(kt1, kv, row_nx, wave, lane, 0, GJ, slot_off);
+  if (n_chunks > 1) gather_chunk<DK>(kt1, kv, row_nx, wave, lane, 0, GJ, slot_off);
   u32 vm_b = (u32)wave_ballot(row_nx >= 0);   // validity of the next chunk
   row_nx = chunk_row(2);                       // rows of the chunk gathered during step 0
   // chunk 0 landed (chunk 1 may be in flight)
   if (n_chunks > 1) {
     if (my_loads == GW_HI) __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI));
-    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI - 1));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI - GW_STEP));
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -345,7 +340,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       s0 = mfma16_bf16(as_v8bf(a0), bq, s0);
       s1 = mfma16_bf16(as_v8bf(a1), bq, s1);
       const int j0 = first_load_at<NKS, GJ>(ks), j1 = first_load_at<NKS, GJ>(ks + 1);
-      if (j0 < j1 && more) gather_chunk<DK, OFF32>(gtile, kv, row_nx, wave, lane, j0, j1, slot_off);
+      if (j0 < j1 && more) gather_chunk<DK>(gtile, kv, row_nx, wave, lane, j0, j1, slot_off);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -422,7 +417,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     // chunk c+1 has landed: only this step's loads (chunk c+2) may still be in flight
     if (more) {
       if (my_loads == GW_HI) __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI));
-      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI - 1));
+      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(GW_HI - GW_STEP));
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
@@ -513,20 +508,14 @@ __global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const uint16_t* __r
 template <int DK, int DV>
 hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  // rows of the KV array, and whether its bytes fit a 31-bit offset
-  const long long kv_rows =
-      a.page_table == nullptr ? (long long)a.n_kv : (long long)a.n_pages * a.page_size;
-  const bool off32 = kv_rows * DK * 2 < (1ll << 31);
   if (a.page_table == nullptr) {
-    auto kern = off32 ? sparse_mqa_kernel<DK, DV, false, true> : sparse_mqa_kernel<DK, DV, false, false>;
-    hipLaunchKernelGGL(kern, dim3(a.n_q, 1), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false>), dim3(a.n_q, 1), dim3(NT), 0, stream,
                        a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, 0, 0, 1, a.n_kv, a.H, a.top_k,
                        scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr);
     return hipGetLastError();
   }
   const int rps = a.rows_per_split;
-  auto kern = off32 ? sparse_mqa_kernel<DK, DV, true, true> : sparse_mqa_kernel<DK, DV, true, false>;
-  hipLaunchKernelGGL(kern, dim3(a.n_q, a.n_split), dim3(NT), 0,
+  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true>), dim3(a.n_q, a.n_split), dim3(NT), 0,
                      stream, a.q, a.kv, a.idx, a.qpos_or_ctx, a.page_table, a.max_pages,
                      a.n_pages, a.page_size, 0, a.H, a.top_k, scale_log2, a.n_split, rps, a.out,
                      a.lse, a.part_o, a.part_ml);
