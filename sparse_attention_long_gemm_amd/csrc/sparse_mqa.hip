@@ -241,21 +241,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   if (r1 > top_k) r1 = top_k;
   const int nrows = r1 > r0 ? r1 - r0 : 0;
 
-  for (int i = tid; i < nrows; i += NT) {
-    const int s = idx[(size_t)qi * top_k + r0 + i];
-    int row = -1;
-    if (s >= 0 && s <= t) {
-      if (PAGED) {
-        const int pg = page_table[(size_t)qi * max_pages + s / page_size];
-        if (pg >= 0 && pg < n_pages) row = pg * page_size + s % page_size;
-      } else {
-        row = s;
-      }
-    }
-    sh.rows[i] = row;
-  }
-
-  // ---- queries: B operand of k-step ks = dims 32ks + 8g .. +8 of head `head` ----
+  // ---- queries: B operand of k-step ks = dims 32ks + 8g .. +8 of head `head` (issued first,
+  // so that their latency overlaps the index and page-table reads below) ----
   v8bf qf[QR];
   {
     const uint16_t* qrow = q + ((size_t)qi * H + (head_ok ? head : 0)) * DK;
@@ -267,6 +254,38 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
         qf[ks < QR ? ks : 0] = as_v8bf(x);
       else
         sh.qs[wave][ks - QR][lane] = as_v8bf(x);
+    }
+  }
+
+  // ---- physical row of every selected entry (-1: skipped); all index reads of a thread are
+  // issued before any is used, then the page-table reads ----
+  {
+    constexpr int RPT = MAX_ROWS / NT;   // entries per thread
+    static_assert(MAX_ROWS % NT == 0, "rows per thread");
+    int sv[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int i = tid + k * NT;
+      sv[k] = i < nrows ? idx[(size_t)qi * top_k + r0 + i] : -1;
+    }
+    int pg[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const bool ok = sv[k] >= 0 && sv[k] <= t;
+      if (PAGED) pg[k] = ok ? page_table[(size_t)qi * max_pages + sv[k] / page_size] : -1;
+      else pg[k] = ok ? 0 : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int i = tid + k * NT;
+      if (i >= nrows) continue;
+      int row = -1;
+      if (PAGED) {
+        if (pg[k] >= 0 && pg[k] < n_pages) row = pg[k] * page_size + sv[k] % page_size;
+      } else if (pg[k] == 0) {
+        row = sv[k];
+      }
+      sh.rows[i] = row;
     }
   }
 

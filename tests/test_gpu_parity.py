@@ -362,6 +362,53 @@ def test_decode_equals_prefill_last_row():
         assert (pl[0] - lse[b]).abs().max().item() <= 1e-4
 
 
+def test_decode_row_longer_than_position_bitmap():
+    """A row of 270000 keys: more positions than the selection's on-chip bitmap covers
+    (2^18), so the selected positions are listed and sorted instead."""
+    sp = gi.DecodeSpec(B=2, idx=gi.IndexerSpec(top_k=2048), mqa=gi.MqaSpec(sigma=1.0),
+                       spare_pages=2, seed=37)
+    d = gi.decode_inputs(sp, ctx_lens=(270000, 3000))
+    step("decode: a row beyond the position bitmap (270000 keys)")
+    idx, o, lse = run_decode(d)
+    torch.cuda.synchronize()
+    i_ref, o_ref, l_ref = orc.decode(d)
+    check_idx(idx, i_ref, "long row idx")
+    check_attn(o, lse, o_ref, l_ref, "long row attn")
+
+
+def test_decode_page_table_entries_outside_the_pool():
+    """Page-table entries outside [0, n_pages) inside a context: the indexer scores their keys
+    as zero keys and the attention skips them.  Reference: the same step with those pages
+    pointing at an all-zero k_I page (indexer), and those positions dropped (attention)."""
+    sp = gi.DecodeSpec(B=3, idx=gi.IndexerSpec(top_k=512), mqa=gi.MqaSpec(sigma=1.0),
+                       spare_pages=2, seed=41)
+    d = gi.decode_inputs(sp, ctx_lens=(3000, 5000, 1000))
+    P, n_pages = d["page_size"], d["n_pages"]
+    bad = [(0, 5, -1), (1, 10, n_pages + 3), (1, 11, 1 << 30), (2, 0, -7)]
+    pt = d["page_table"].clone()
+    for b, j, v in bad:
+        pt[b, j] = v
+    d_bad = dict(d, page_table=pt)
+    step("decode: page-table entries outside the pool")
+    idx, o, lse = run_decode(d_bad)
+    torch.cuda.synchronize()
+    # indexer reference: the bad entries point at an extra all-zero k_I page
+    pt_z = pt.clone()
+    for b, j, v in bad:
+        pt_z[b, j] = n_pages
+    kz = torch.cat([d["k_cache"], torch.zeros_like(d["k_cache"][:1])])
+    d_z = dict(d, page_table=pt_z, k_cache=kz)
+    i_ref, _, _ = orc.decode(d_z)
+    check_idx(idx, i_ref, "bad pages idx")
+    # attention reference: positions on bad pages are not attended
+    drop = np.array(i_ref, copy=True)
+    for b, j, v in bad:
+        on_bad = (drop[b] >= j * P) & (drop[b] < (j + 1) * P)
+        drop[b][on_bad] = -1
+    _, o_ref, l_ref = orc.decode(d_bad, idx=drop)
+    check_attn(o, lse, o_ref, l_ref, "bad pages attn")
+
+
 def test_decode_full_batch64_sampled():
     """Paged decode, batch 64, ctx ~ U[4096, 131072], page size 64, random page tables."""
     sp = gi.DecodeSpec()
