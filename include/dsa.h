@@ -91,7 +91,10 @@ dsa_status dsa_indexer_topk(const uint8_t* q_idx, const float* w, const uint8_t*
  * k_cache    [n_pages, page_size, d_I]   FP8   logical row s of sequence b lives at
  *                                              page page_table[b*max_pages + s/page_size],
  *                                              slot s % page_size
- * page_table [B, max_pages]              int32 entries beyond the context are not read
+ * page_table [B, max_pages]              int32 entries beyond the context are not read;
+ *                                              an entry outside [0, n_pages) inside the
+ *                                              context is read as a page of all-zero keys
+ *                                              (score 0), never out of bounds
  * ctx_lens   [B]                         int32 context length (>= 0, <= max_pages*page_size);
  *                                              candidates are s in [0, ctx)
  * out_idx    [B, top_k]                  int32 logical positions, ascending, then -1
