@@ -335,32 +335,53 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     }
   }
 
-  // ---- key tile loads: thread -> (key row lr = tid / 4, 32-byte half-pair hp = tid % 4) ----
-  const int lr = tid >> 2, lc = 2 * (tid & 3);  // logical 16-byte chunks lc, lc+1
-  auto load_tile = [&](int it_, v4i& c0, v4i& c1) {
-    const int s = it_ * BK2 + lr;
-    const bool ok = s < n_keys;
-    c0 = v4i{0, 0, 0, 0};
-    c1 = v4i{0, 0, 0, 0};
-    if (ok && 16 * lc < d_I) c0 = load16(k_idx + (size_t)s * d_I + 16 * lc);
-    if (ok && 16 * lc + 16 < d_I) c1 = load16(k_idx + (size_t)s * d_I + 16 * lc + 16);
-  };
-  auto store_tile = [&](int b, const v4i& c0, const v4i& c1) {
-    *reinterpret_cast<v4i*>(&sh.ktile[b][lr * 128 + 16 * kchunk(lr, lc)]) = c0;
-    *reinterpret_cast<v4i*>(&sh.ktile[b][lr * 128 + 16 * kchunk(lr, lc + 1)]) = c1;
+  // ---- key tiles straight from global memory into LDS (global_load_lds, 16 bytes per lane):
+  // wave-load j (0..15) of a tile fills bytes [1024 j, 1024 j + 1024), i.e. rows 8j .. 8j+7;
+  // lane L fills physical chunk L % 8 of row 8j + L / 8, which holds logical chunk
+  // (L % 8) ^ ((row >> 1) & 7) (the kchunk swizzle).  Wave w issues wave-loads w and w + 8,
+  // whose rows have the same (row >> 1) & 7 pattern.  Keys past n_keys and chunks past d_I
+  // are not loaded: the tiles are zeroed once, so chunks past d_I stay zero, and a key past
+  // n_keys (whose slot may hold an older key) is past every row's last position t. ----
+  const int dl_row = lane >> 3;
+  const int dl_chunk = (lane & 7) ^ ((4 * (wave & 1) + (dl_row >> 1)) & 7);
+  const bool dl_chunk_ok = 16 * dl_chunk < d_I;
+  const u32 dl_off = (u32)(dl_row * d_I + 16 * dl_chunk);
+  auto dma_tile = [&](int it_, int b) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = __builtin_amdgcn_readfirstlane(wave) + NWAVE * jj;   // wave-uniform
+      const int s0 = __builtin_amdgcn_readfirstlane(it_ * BK2 + 8 * j);
+      // 64-bit base in scalar registers: each half through readfirstlane (which returns a
+      // signed int), widened as unsigned so the low half is not sign-extended
+      const uint64_t bp = (uint64_t)(uintptr_t)(k_idx + (size_t)s0 * d_I);
+      const uint64_t base =
+          ((uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)(bp >> 32)) << 32) |
+          (uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)bp);
+      const u32 lds = __builtin_amdgcn_readfirstlane(
+          (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(sh.ktile[b] + 1024 * j));
+      if (dl_chunk_ok && s0 + dl_row < n_keys) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                     :
+                     : "v"(dl_off), "s"(lds), "s"(base)
+                     : "memory", "m0");
+#pragma clang diagnostic pop
+      }
+    }
   };
 
   const int n_iter = (t_max + BK2) / BK2;  // key tiles covering keys 0..t_max
-  {
-    v4i c0, c1;
-    load_tile(0, c0, c1);
-    store_tile(0, c0, c1);
-  }
+  for (int i = tid; i < 2 * BK2 * 128 / 16; i += NT)
+    reinterpret_cast<v4i*>(&sh.ktile[0][0])[i] = v4i{0, 0, 0, 0};
+  __syncthreads();
+  dma_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // Scores of key tile `kt` (keys [128 kt, 128 kt + 128)) from key buffer kt%2 into partial
-  // buffer kt%2, then the next tile (already in registers) into the other key buffer.
-  auto compute = [&](int kt, const v4i& nc0, const v4i& nc1) {
+  // buffer kt%2.
+  auto compute = [&](int kt) {
     const int buf = kt & 1;
     const uint8_t* tile = sh.ktile[buf] + kh * BK * 128;
 #pragma unroll
@@ -384,7 +405,6 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       if (f == hg)
         *reinterpret_cast<v4f*>(&sh.plin[buf][kh][c16][16 * f + 4 * g]) = linear_term(a, sh, lane);
     }
-    if (kt + 1 < n_iter) store_tile(buf ^ 1, nc0, nc1);
   };
 
   // This wave's rows over key tile `kt`: I = (sum_j w_j x_j + sum_j w_j |x_j|) / 2 =
@@ -464,18 +484,19 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       }
     }
 
-    // ---- fetch the next key tile into registers (stored to LDS after the MFMA work) ----
-    v4i nc0 = {0, 0, 0, 0}, nc1 = {0, 0, 0, 0};
-    if (it + 1 < n_iter) load_tile(it + 1, nc0, nc1);
+    // ---- the next key tile into the other key buffer (read in the previous step); it has
+    // landed by the end of this step ----
+    if (it + 1 < n_iter) dma_tile(it + 1, (it + 1) & 1);
 
 #pragma unroll 1
     for (int ph = 0; ph < 2; ++ph) {
       if (ph == kh) {
-        if (it < n_iter) compute(it, nc0, nc1);
+        if (it < n_iter) compute(it);
       } else {
         if (kf >= 0) filter(kf);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next key tile has landed
     __syncthreads();
   }
 
