@@ -64,6 +64,20 @@ def test_indexer_production_heads_ragged(L, top_k, n_q0):
     check_idx(got, orc.prefill_indexer_topk(d), f"L={L} k={top_k}")
 
 
+@pytest.mark.parametrize("L,H_I,d_I,top_k,n_q0", [(700, 7, 48, 64, 5), (1000, 33, 80, 200, 0),
+                                                  (389, 64, 112, 100, 77)])
+def test_indexer_other_dims(L, H_I, d_I, top_k, n_q0):
+    """Key rows of 48, 80 and 112 bytes (partial 128-byte tiles), head counts that leave head
+    groups partly or wholly empty, key and row counts off the tile sizes."""
+    wl = gi.Workload(name="dims", L=L, idx=gi.IndexerSpec(H_I=H_I, d_I=d_I, top_k=top_k),
+                     mqa=None, seed=17)
+    d = gi.prefill_inputs(wl, rows=(n_q0, L - n_q0), with_mqa=False)
+    step(f"indexer L={L} H_I={H_I} d_I={d_I} k={top_k}")
+    got = run_indexer(d)
+    torch.cuda.synchronize()
+    check_idx(got, orc.prefill_indexer_topk(d), f"H_I={H_I} d_I={d_I}")
+
+
 def test_indexer_ties_everywhere():
     """Operands in {0, 1/8} with unit weights: scores are small multiples of 2^-6, so nearly
     every row has a large tie at its threshold and the lowest-position rule decides it."""
