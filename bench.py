@@ -204,6 +204,12 @@ def measured_ceilings(dsa, dev, reps: int = 3):
         best = max(best, nb / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     out["hbm_read_gbps"] = best
     del src
+    # the shader clock these MFMA rates imply: a SIMD retires 1024 bf16 or 2048 FP8 flop per
+    # cycle on these shapes (32x32x16 bf16 in 32 cycles, 16x16x128 FP8 in 32 cycles)
+    simds = 4 * n_cu
+    out["implied_mfma_clock_ghz"] = {
+        "bf16": out["bf16_mfma_tflops"] * 1e12 / (simds * 1024) / 1e9,
+        "fp8": out["fp8_mfma_tflops"] * 1e12 / (simds * 2048) / 1e9}
     out["kernels"] = ("dsa_ceiling_mfma (32x32x16 bf16 / 16x16x128 FP8 chains, "
                       f"{n_wg} workgroups x 8 waves) and dsa_ceiling_read (4 GiB, nt loads)")
     return out
