@@ -25,7 +25,8 @@
 // logits breaks the bound.
 //
 // Decode (paged) splits each sequence's selected rows over n_split workgroups; partial
-// (unnormalised o, running max, running sum) triples are merged by mqa_combine_kernel.
+// (output normalised by the split's own sum, running max, running sum) are merged by
+// mqa_combine_kernel.
 #include "dsa_common.hpp"
 #include "dsa_kernels.hpp"
 
@@ -488,8 +489,9 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 
 // Merge the n_split partial results of one (query, head): partial i holds o_i / l_i (bf16) with
 // its running max m_i and sum l_i, so o = sum_i w_i (o_i / l_i) / sum_i w_i with
-// w_i = exp2(m_i - M) l_i.  One workgroup per (query, head); each thread owns 4 consecutive dims.
-template <int DV>
+// w_i = exp2(m_i - M) l_i.  One workgroup per (query, head); each thread owns 4 consecutive dims
+// and issues the reads of every partial before using any (one memory round trip).
+template <int DV, int MAXS>
 __global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const uint16_t* __restrict__ part_o,
                                                              const float* __restrict__ part_ml,
                                                              int H, int n_split,
@@ -498,21 +500,37 @@ __global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const uint16_t* __r
   const int qi = blockIdx.x / H;
   const int h = blockIdx.x - qi * H;
   const size_t base = (size_t)qi * n_split * H + h;   // partial i lives at base + i*H
+  const int d = 4 * threadIdx.x;
+  float mv[MAXS], lv[MAXS];
+  uint2 ov[MAXS];
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    mv[i] = -__builtin_inff();
+    lv[i] = 0.f;
+    ov[i] = uint2{0u, 0u};
+    if (i < n_split) {
+      const size_t b = base + (size_t)i * H;
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + b * 2);
+      mv[i] = ml.x;
+      lv[i] = ml.y;
+      ov[i] = *reinterpret_cast<const uint2*>(part_o + b * DV + d);
+    }
+  }
   float M = -__builtin_inff();
-  for (int i = 0; i < n_split; ++i) M = fmaxf(M, part_ml[(base + (size_t)i * H) * 2]);
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) M = fmaxf(M, mv[i]);
   float L = 0.f;
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  const int d = 4 * threadIdx.x;
   if (M != -__builtin_inff()) {
-    for (int i = 0; i < n_split; ++i) {
-      const size_t b = base + (size_t)i * H;
-      const float wgt = exp2f(part_ml[b * 2] - M) * part_ml[b * 2 + 1];
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      if (i >= n_split) break;
+      const float wgt = exp2f(mv[i] - M) * lv[i];
       L += wgt;
-      const uint2 v = *reinterpret_cast<const uint2*>(part_o + b * DV + d);
-      acc[0] += wgt * bf16_to_f32((uint16_t)(v.x & 0xffffu));
-      acc[1] += wgt * bf16_to_f32((uint16_t)(v.x >> 16));
-      acc[2] += wgt * bf16_to_f32((uint16_t)(v.y & 0xffffu));
-      acc[3] += wgt * bf16_to_f32((uint16_t)(v.y >> 16));
+      acc[0] += wgt * bf16_to_f32((uint16_t)(ov[i].x & 0xffffu));
+      acc[1] += wgt * bf16_to_f32((uint16_t)(ov[i].x >> 16));
+      acc[2] += wgt * bf16_to_f32((uint16_t)(ov[i].y & 0xffffu));
+      acc[3] += wgt * bf16_to_f32((uint16_t)(ov[i].y >> 16));
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -540,8 +558,13 @@ hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
                      a.lse, a.part_o, a.part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL((mqa_combine_kernel<DV>), dim3(a.n_q * a.H), dim3(DV / 4), 0, stream,
-                     a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
+  // partial counts up to the ABI's limit of 16 splits
+  if (a.n_split <= 4)
+    hipLaunchKernelGGL((mqa_combine_kernel<DV, 4>), dim3(a.n_q * a.H), dim3(DV / 4), 0, stream,
+                       a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
+  else
+    hipLaunchKernelGGL((mqa_combine_kernel<DV, 16>), dim3(a.n_q * a.H), dim3(DV / 4), 0,
+                       stream, a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
   return hipGetLastError();
 }
 
