@@ -491,7 +491,11 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 #pragma unroll 1
     for (int ph = 0; ph < 2; ++ph) {
       if (ph == kh) {
+        // the scoring phase issues ahead of the other wave's filter on the SIMD, which keeps
+        // the matrix pipe fed while the filter's VALU work fills the gaps
+        __builtin_amdgcn_s_setprio(1);
         if (it < n_iter) compute(it);
+        __builtin_amdgcn_s_setprio(0);
       } else {
         if (kf >= 0) filter(kf);
       }
