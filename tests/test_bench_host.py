@@ -1,0 +1,36 @@
+"""Host-side logic of bench.py (CPU only): the single-GPU guard and the rule that a recorded HBM
+traffic figure is reported only while the kernel sources it was taken on are unchanged."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""          # no JSON line for a refused run
+
+
+def test_traffic_is_reported_only_for_unchanged_sources(monkeypatch):
+    with open(bench.TRAFFIC_FILE) as fh:
+        stored = json.load(fh)["kernels"]
+    for kernel in bench.KERNEL_SOURCES:
+        rec = stored[kernel]
+        monkeypatch.setattr(bench, "source_digest", lambda k, d=rec["source_sha256"]: d)
+        assert bench.recorded_traffic(kernel) == rec["bytes_per_launch"] > 0
+        monkeypatch.setattr(bench, "source_digest", lambda k: "0" * 64)
+        assert bench.recorded_traffic(kernel) is None
+
+
+def test_source_digest_covers_every_listed_file():
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        for f in files:
+            assert os.path.isfile(os.path.join(bench.CSRC, f)), (kernel, f)
+        assert len(bench.source_digest(kernel)) == 64
