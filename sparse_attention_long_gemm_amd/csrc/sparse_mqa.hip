@@ -8,7 +8,7 @@
 //
 // One workgroup = one query row (all heads) x one slice of its selected rows, 8 waves.  Wave w
 // owns heads 16w .. 16w+15 over all dimensions (v_mfma_f32_16x16x32_bf16): its queries stay
-// in registers as the B operand of S^T = K Q^T (the last k-steps in LDS) and its fp32 output
+// in registers as the B operand of S^T = K Q^T (all 18 k-steps at DK = 576) and its fp32 output
 // accumulators O^T stay in registers for the whole slice, so the waves never exchange partial
 // results and every probability is computed once.  The selected rows are gathered 32 at a
 // time straight from global memory into a ring of three LDS tiles (global_load_lds, 16 bytes
@@ -88,16 +88,7 @@ __device__ __forceinline__ v4f mfma16_bf16(const v8bf& a, const v8bf& b, const v
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DK>
-struct QSplit {
-  static constexpr int NKS = DK / 32;
-  static constexpr int QL = NKS >= 16 ? 4 : 0;   // k-steps of the queries kept in LDS
-  static constexpr int QR = NKS - QL;
-};
-
-template <int DK>
 struct MqaShared {
-  alignas(16) v8bf qs[NW][QSplit<DK>::QL > 0 ? QSplit<DK>::QL : 1][kWave];
   int rows[MAX_ROWS];   // physical row of each selected entry, or -1
 };
 
@@ -207,12 +198,11 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml) {
   static_assert(DK % 32 == 0 && DV % 16 == 0 && DV <= DK, "shape");
-  using Sh = MqaShared<DK>;
+  using Sh = MqaShared;
   constexpr int NKS = DK / 32;           // k-steps of the S^T product
   constexpr int NDB = DV / 16;           // 16-dim blocks of the output
   constexpr int RS = Tile<DK>::RS;
   constexpr int GJ = Tile<DK>::GJ;
-  constexpr int QR = QSplit<DK>::QR;
   __shared__ Sh sh;
   __shared__ __attribute__((aligned(16))) uint8_t kt0[Tile<DK>::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t kt1[Tile<DK>::BYTES];
@@ -244,17 +234,14 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 
   // ---- queries: B operand of k-step ks = dims 32ks + 8g .. +8 of head `head` (issued first,
   // so that their latency overlaps the index and page-table reads below) ----
-  v8bf qf[QR];
+  v8bf qf[NKS];
   {
     const uint16_t* qrow = q + ((size_t)qi * H + (head_ok ? head : 0)) * DK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       v4i x = {0, 0, 0, 0};
       if (head_ok) x = ld16(qrow + 32 * ks + 8 * g);
-      if (ks < QR)
-        qf[ks < QR ? ks : 0] = as_v8bf(x);
-      else
-        sh.qs[wave][ks - QR][lane] = as_v8bf(x);
+      qf[ks] = as_v8bf(x);
     }
   }
 
@@ -308,7 +295,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   const int my_loads = gather_count<DK>(wave) * gather_insts<DK>();
   int slot_off[GJ];
   gather_plan<DK>(wave, lane, slot_off);
-  __syncthreads();   // rows[] and the LDS queries complete
+  __syncthreads();   // rows[] complete
   int row_nx = chunk_row(0);
   if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane, 0, GJ, slot_off);
   u32 vm_a = (u32)wave_ballot(row_nx >= 0);   // validity of the chunk being computed
@@ -344,18 +331,16 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const lds_u8* b0 = tile + qk_off0;
     const lds_u8* b1 = tile + qk_off1;
     v4i ka[QPD], kb[QPD];
-    v8bf kq[QPD];
     auto fetch = [&](int k) {
       ka[k % QPD] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(b0 + 64 * k);
       kb[k % QPD] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(b1 + 64 * k);
-      if (k >= QR) kq[k % QPD] = sh.qs[wave][k >= QR ? k - QR : 0][lane];
     };
 #pragma unroll
     for (int ks = 0; ks < QPD && ks < NKS; ++ks) fetch(ks);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const v4i a0 = ka[ks % QPD], a1 = kb[ks % QPD];
-      const v8bf bq = ks < QR ? qf[ks < QR ? ks : 0] : kq[ks % QPD];
+      const v8bf bq = qf[ks];
       if (ks + QPD < NKS) fetch(ks + QPD);
       s0 = mfma16_bf16(as_v8bf(a0), bq, s0);
       s1 = mfma16_bf16(as_v8bf(a1), bq, s1);
