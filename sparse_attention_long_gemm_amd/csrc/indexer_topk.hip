@@ -389,15 +389,18 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       const v8i a = frag_from_tile(tile, 16 * f + c16, g);
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
       if (heads_here) {
-        // software-pipelined: MFMA j+1 is issued before the epilogue of MFMA j
-        v4f x = mfma_fp8(a, qf[0]);
+        // software-pipelined: the epilogue of MFMA j follows the issue of MFMA j+2, so a
+        // lone wave does not stall on each result (about 0.7 of the matrix rate with the
+        // epilogue one MFMA behind, 0.8 with it two behind, measured); the barrier keeps the
+        // compiler from pulling the epilogues earlier
+        constexpr int PD = 3;
+        v4f x[PD + 1];
 #pragma unroll
-        for (int j = 1; j < HPW; ++j) {
-          const v4f xn = mfma_fp8(a, qf[j]);
-          epi_abs(acc, x, wv[j - 1]);
-          x = xn;
+        for (int j = 0; j < HPW + PD; ++j) {
+          if (j < HPW) x[j % (PD + 1)] = mfma_fp8(a, qf[j]);
+          if (j >= PD) epi_abs(acc, x[(j - PD) % (PD + 1)], wv[j - PD]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        epi_abs(acc, x, wv[HPW - 1]);
       }
       *reinterpret_cast<v4f*>(&sh.part[buf][kh][hg][c16][16 * f + 4 * g]) =
           v4f{acc[0], acc[1], acc[2], acc[3]};
