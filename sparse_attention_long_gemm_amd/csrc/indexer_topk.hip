@@ -426,30 +426,36 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
         scv[rr][half] = 0.5f * (sh.plin[buf][half][r][lane] + ab);
       }
     }
+    bool ps[RPW][2];
+    uint64_t mk[RPW][2];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int t = t_own[rr];
+      const bool live = q0 + RPW * wave + rr < n_q && kt * BK2 <= t;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        ps[rr][half] = live && (kt * BK2 + half * BK + lane <= t) && (scv[rr][half] > thr[rr]);
+        mk[rr][half] = wave_ballot(ps[rr][half]);
+      }
+    }
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       const int r = RPW * wave + rr;
       const int q = q0 + r;
-      const int t = t_own[rr];
-      if (q >= n_q || kt * BK2 > t) continue;
+      const int c0 = __builtin_popcountll(mk[rr][0]);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int s = kt * BK2 + half * BK + lane;
-        const float sc = scv[rr][half];
-        const bool pass = (s <= t) && (sc > thr[rr]);
-        const uint64_t m = wave_ballot(pass);
-        if (m != 0ull) {
-          if (pass) {
-            const u32 key = ord_key(sc);
-            hi_seen[rr] = max(hi_seen[rr], key);
-            const int p = cnt[rr] + lanes_below(m);
-            cand_score[(size_t)q * cap + p] = (sc == 0.f) ? 0.f : sc;
-            cand_pos[(size_t)q * cap + p] = s;
-            if (rowh[rr].valid) atomicAdd(&sh.rhist[r][hbin(key, rowh[rr])], 1u);
-          }
-          cnt[rr] += __builtin_popcountll(m);
+        if (ps[rr][half]) {
+          const float sc = scv[rr][half];
+          const u32 key = ord_key(sc);
+          hi_seen[rr] = max(hi_seen[rr], key);
+          const int p = cnt[rr] + (half ? c0 : 0) + lanes_below(mk[rr][half]);
+          cand_score[(size_t)q * cap + p] = (sc == 0.f) ? 0.f : sc;
+          cand_pos[(size_t)q * cap + p] = kt * BK2 + half * BK + lane;
+          if (rowh[rr].valid) atomicAdd(&sh.rhist[r][hbin(key, rowh[rr])], 1u);
         }
       }
+      cnt[rr] += c0 + __builtin_popcountll(mk[rr][1]);
     }
     bool full = false;
 #pragma unroll
