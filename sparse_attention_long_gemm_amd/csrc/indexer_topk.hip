@@ -220,16 +220,16 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(int lo, int hi) {
 // k-step ks of lane group g covers dims 16g + 8ks .. +8 (ks < 2) and 64 + 16g + 8(ks-2) .. +8,
 // the dims of the FP8 fragments.
 __device__ __forceinline__ v4f linear_term(const v8i& a, const PrefillShared& sh, int lane) {
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const v8bf ab = fp8x8_to_bf16(a[2 * ks], a[2 * ks + 1]);
 #pragma unroll
     for (int pc = 0; pc < 3; ++pc)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          ab, *reinterpret_cast<const v8bf*>(&sh.qlin[pc][ks][lane][0]), acc, 0, 0, 0);
+      acc[(3 * ks + pc) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          ab, *reinterpret_cast<const v8bf*>(&sh.qlin[pc][ks][lane][0]), acc[(3 * ks + pc) & 1], 0, 0, 0);
   }
-  return acc;
+  return acc[0] + acc[1];
 }
 
 // Key fragment (16 keys x 32 bytes per lane group) of tile row r0.. from the LDS key tile.
