@@ -75,7 +75,9 @@ class Prefill:
                           selected_pairs_range(a, e, self.top_k) for a, e in self.blocks]
         del d
 
-    def run(self, events=None):
+    def run(self, events=None, after_block=None):
+        """All blocks, in order.  ``after_block(bi, a, e, idx)`` (tests) is called after each
+        block's two launches with that block's index rows (overwritten by the next block)."""
         d, dsa = self.inp, self.dsa
         for bi, (a, e) in enumerate(self.blocks):
             if events is not None:
@@ -89,6 +91,8 @@ class Prefill:
                                    lse=self.lse[a:e])
             if events is not None:
                 events[bi][2].record()
+            if after_block is not None:
+                after_block(bi, a, e, self.idx[: e - a])
 
 
 class Decode:
@@ -219,11 +223,14 @@ def cpu_baseline(prefill: Prefill, budget_s: float = 20.0):
     """The fp64 oracle (as it stands) on a strided sample of the 128K prefill's rows, timed on
     this host; extrapolated to all rows by the exact per-row work model."""
     from oracle import dsa_oracle as orc
+    # the cores this process may run on; the BLAS pools are pinned to that many threads so the
+    # reported count is the one the oracle actually used
+    threads = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
     except Exception:  # pragma: no cover
-        threads = 1
+        limiter = None
     d = prefill.inp
     wl = prefill.wl
     host = {"q_idx": d["q_idx"].cpu(), "w": d["w"].cpu(), "k_idx": d["k_idx"].cpu(),
@@ -245,6 +252,8 @@ def cpu_baseline(prefill: Prefill, budget_s: float = 20.0):
         t_used = time.perf_counter() - t0
         if t_used > budget_s:
             break
+    if limiter is not None:
+        limiter.unregister()
     w_full = sum(work(t) for t in range(L))
     t_full = t_used * w_full / w_done
     return {"value": L / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",

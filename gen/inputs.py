@@ -58,6 +58,13 @@ def choice_f32(shape, choices, seed: int, tensor_id: int, device="cpu"):
     return table[pick]
 
 
+def uniform_f32(shape, lo: float, hi: float, seed: int, tensor_id: int, device="cpu"):
+    """Values uniform in [lo, hi) (fp32): weights off the dyadic grid."""
+    g = _gen(seed, tensor_id, device)
+    u = torch.rand(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    return u * (hi - lo) + lo
+
+
 def normal_bf16(shape, sigma: float, seed: int, tensor_id: int, device="cpu"):
     """N(0, sigma^2) rounded to bf16, filled slice by slice along dim 0."""
     g = _gen(seed, tensor_id, device)

@@ -214,7 +214,7 @@ def prefill(inp: dict, rows=None, idx=None):
 
 
 def paged_gather(cache, page_table_row, positions, page_size: int) -> np.ndarray:
-    """Logical rows ``positions`` of one sequence from a paged cache (host copy; bf16 as bits).
+    """Logical rows ``positions`` of one sequence from a paged cache, on the host (bf16 as bits).
 
     Row s lives at page page_table_row[s // page_size], slot s % page_size.  Paging with
     page size 64 is the serving layout named on the mundobytes.com page (section "Quick guide
@@ -224,15 +224,7 @@ def paged_gather(cache, page_table_row, positions, page_size: int) -> np.ndarray
     pt = _np(page_table_row).astype(np.int64)
     s = np.asarray(positions, dtype=np.int64)
     pages, slots = pt[s // page_size], s % page_size
-    try:
-        import torch
-        if isinstance(cache, torch.Tensor):     # gather on the tensor's device, copy the rows
-            dev = cache.device
-            rows = cache[torch.as_tensor(pages, device=dev), torch.as_tensor(slots, device=dev)]
-            return _np(rows)
-    except ImportError:  # pragma: no cover
-        pass
-    return np.asarray(cache)[pages, slots]
+    return _np(cache)[pages, slots]
 
 
 def paged_rows(cache, page_table_row, n: int, page_size: int) -> np.ndarray:
@@ -254,8 +246,8 @@ def decode(inp: dict, seqs=None, idx=None):
     seqs = list(range(ctx.shape[0])) if seqs is None else list(seqs)
     q_i_all = decode_e4m3fn(inp["q_idx"])
     w_all = _np(inp["w"]).astype(np.float64)
-    kc = inp["k_cache"]
-    kvc = inp["kv_cache"]
+    kc = _np(inp["k_cache"])            # host copies (a device cache is copied over once)
+    kvc = _np(inp["kv_cache"])
     H = inp["q"].shape[1]
     out_idx = np.empty((len(seqs), k), dtype=np.int32)
     o = np.empty((len(seqs), H, d_v))

@@ -96,13 +96,17 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtypes, ndim: int, device=None):
+def _need(t: torch.Tensor, name: str, dtypes, ndim: int, device=None, shape=None):
+    """Check a tensor argument: type, dtype, rank, device memory, contiguity, and (for caller
+    supplied outputs) the exact shape the kernels will write."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
     if t.dim() != ndim:
         raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device (HIP) tensor")
     if not t.is_contiguous():
@@ -122,9 +126,16 @@ def _workspace(nbytes: int, device, workspace):
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    elif workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace of {workspace.numel() * workspace.element_size()} bytes "
-                         f"< required {nbytes}")
+    else:
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace must be a torch.Tensor")
+        if not workspace.is_cuda or workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, expected {device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace of {workspace.numel() * workspace.element_size()} "
+                             f"bytes < required {nbytes}")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -146,7 +157,7 @@ def indexer_topk(q_idx, w, k_idx, q_pos, top_k: int, out=None, workspace=None):
         raise ValueError("inconsistent indexer shapes")
     if out is None:
         out = torch.empty((n_q, top_k), dtype=torch.int32, device=dev)
-    _need(out, "out", _I32, 2, dev)
+    _need(out, "out", _I32, 2, dev, shape=(n_q, top_k))
     ws, nb = _workspace(indexer_topk_workspace_size(n_q, top_k), dev, workspace)
     _check(lib.dsa_indexer_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), k_idx.shape[0], _ptr(q_pos),
                                 n_q, H_I, d_I, top_k, _ptr(out), _ptr(ws), nb, _stream(dev)),
@@ -175,7 +186,7 @@ def indexer_topk_paged(q_idx, w, k_cache, page_table, ctx_lens, top_k: int, out=
         raise ValueError("inconsistent paged indexer shapes")
     if out is None:
         out = torch.empty((B, top_k), dtype=torch.int32, device=dev)
-    _need(out, "out", _I32, 2, dev)
+    _need(out, "out", _I32, 2, dev, shape=(B, top_k))
     ws, nb = _workspace(indexer_topk_paged_workspace_size(B, max_pages, page_size), dev, workspace)
     _check(lib.dsa_indexer_topk_paged(_ptr(q_idx), _ptr(w), _ptr(k_cache), _ptr(page_table),
                                       _ptr(ctx_lens), B, max_pages, n_pages, page_size, H_I, d_I,
@@ -201,7 +212,9 @@ def sparse_mqa_prefill(q, kv, idx, q_pos, d_v: int, scale: float, out=None, lse=
         out = torch.empty((n_q, H, d_v), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((n_q, H), dtype=torch.float32, device=dev)
-    _need(out, "out", _BF16, 3, dev)
+    _need(out, "out", _BF16, 3, dev, shape=(n_q, H, d_v))
+    if lse is not None:
+        _need(lse, "lse", _F32, 2, dev, shape=(n_q, H))
     _check(lib.dsa_sparse_mqa_prefill(_ptr(q), _ptr(kv), kv.shape[0], _ptr(idx), _ptr(q_pos),
                                       n_q, H, D_k, d_v, idx.shape[1], float(scale), _ptr(out),
                                       _ptr(lse), _stream(dev)),
@@ -233,6 +246,9 @@ def sparse_mqa_decode(q, kv_cache, page_table, ctx_lens, idx, d_v: int, scale: f
         out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", _BF16, 3, dev, shape=(B, H, d_v))
+    if lse is not None:
+        _need(lse, "lse", _F32, 2, dev, shape=(B, H))
     ws, nb = _workspace(sparse_mqa_decode_workspace_size(B, H, d_v, top_k, n_split), dev,
                         workspace)
     _check(lib.dsa_sparse_mqa_decode(_ptr(q), _ptr(kv_cache), _ptr(page_table), _ptr(ctx_lens),

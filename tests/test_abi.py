@@ -70,7 +70,7 @@ def test_workspace_sizes():
     rs = 2048 * 64
     assert lib.dsa_indexer_topk_paged_workspace_size(64, 2048, 64) == \
         3 * 64 * rs * 4 + 64 * 4096 * 4 + 1024 + 64 * 2048 * 4
-    # B=64, top_k=2048 -> 4 splits of 512 rows: partial o (fp32) + (max, sum) per head
+    # B=64, top_k=2048 -> 4 splits of 512 rows: partial o (bf16) + (max, sum) in fp32 per head
     assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 2048, 0) == 64 * 4 * 128 * (512 * 2 + 8)
     assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 2048, 1) == 0
     assert lib.dsa_sparse_mqa_decode_workspace_size(64, 128, 512, 32, 0) == 0
@@ -145,3 +145,21 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         dsa.indexer_topk(x, torch.zeros((4, 4)), torch.zeros((8, 32), dtype=torch.uint8),
                          torch.zeros(4, dtype=torch.int32), 8)
+
+
+def test_binding_output_and_workspace_checks():
+    """The binding's argument checks (run on host tensors, no GPU needed): an output of the
+    wrong shape and a workspace that is not device memory are refused."""
+    import torch
+    from sparse_attention_long_gemm_amd import _need, _workspace
+    out = torch.empty((3, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="expected shape"):
+        _need(out, "out", (torch.int32,), 2, shape=(3, 5))
+    with pytest.raises(TypeError):
+        _need(out, "out", (torch.float32,), 2, shape=(3, 4))
+    with pytest.raises(ValueError, match="device"):
+        _need(out, "out", (torch.int32,), 2, shape=(3, 4))       # host tensor
+    with pytest.raises(ValueError, match="expected cuda"):
+        _workspace(64, torch.device("cuda", 0), torch.empty(128, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        _workspace(64, torch.device("cuda", 0), bytearray(128))
