@@ -53,7 +53,8 @@ typedef enum dsa_status {
   DSA_ERR_INVALID_ARG = -1,       /* null required pointer, negative size, bad page size... */
   DSA_ERR_UNSUPPORTED_SHAPE = -2, /* no kernel instance for this (H_I, d_I, H, D_k, D_v, k)  */
   DSA_ERR_WORKSPACE_TOO_SMALL = -3,
-  DSA_ERR_HIP = -4                /* a launch failed (hipGetLastError after the launch)     */
+  DSA_ERR_HIP = -4,               /* a launch failed (hipGetLastError after the launch)     */
+  DSA_ERR_SCRATCH_LIMIT = -5      /* the allocation-free entry point's scratch is too small */
 } dsa_status;
 
 /* ABI version of the loaded library (DSA_ABI_VERSION at build time). */
@@ -145,6 +146,33 @@ dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
                                  int32_t D_v, int32_t top_k, float scale, int32_t n_split,
                                  uint16_t* out, float* lse, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Allocation-free variant of dsa_sparse_mqa_decode, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, layouts, checks, kernels and results as dsa_sparse_mqa_decode, without the
+ * workspace: the split partials live in a static device array of DSA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends (its address on each
+ * device is looked up once, on the first call there).  The call never allocates or frees.
+ *  - A call whose partials need more than DSA_NOALLOC_SCRATCH_BYTES (the size
+ *    dsa_sparse_mqa_decode_workspace_size reports for the same B, H, D_v, top_k, n_split)
+ *    returns DSA_ERR_SCRATCH_LIMIT and enqueues nothing.  At H=128, D_v=512 the limit holds
+ *    B * n_split <= 508 (e.g. B=64 with the library's 4 splits, or B=127 with 4).
+ *  - Every call on one GPU shares that GPU's array: calls whose executions overlap on the
+ *    same GPU (different streams, or host threads racing) race on it and give undefined
+ *    results.  Calls ordered on one stream are safe: each writes every partial it reads, so
+ *    nothing carries over from the previous call.
+ * ------------------------------------------------------------------------------------- */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+dsa_status dsa_sparse_mqa_decode_noalloc(const uint16_t* q, const uint16_t* kv_cache,
+                                         const int32_t* page_table, const int32_t* ctx_lens,
+                                         const int32_t* idx, int32_t B, int32_t max_pages,
+                                         int32_t n_pages, int32_t page_size, int32_t H,
+                                         int32_t D_k, int32_t D_v, int32_t top_k, float scale,
+                                         int32_t n_split, uint16_t* out, float* lse,
+                                         hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Measurement helpers (not part of the path).  They report what this GPU sustains on the

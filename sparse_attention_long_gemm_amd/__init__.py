@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
 DSA_OK = 0
 _STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED_SHAPE",
-           -3: "DSA_ERR_WORKSPACE_TOO_SMALL", -4: "DSA_ERR_HIP"}
+           -3: "DSA_ERR_WORKSPACE_TOO_SMALL", -4: "DSA_ERR_HIP", -5: "DSA_ERR_SCRATCH_LIMIT"}
 
 # Every exported symbol of include/dsa.h, with its ctypes signature.
 _P, _I, _Z, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
@@ -42,6 +42,8 @@ SIGNATURES = {
     "dsa_sparse_mqa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "dsa_sparse_mqa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                              _F, _I, _P, _P, _P, _Z, _P]),
+    "dsa_sparse_mqa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                                     _I, _I, _I, _F, _I, _P, _P, _P]),
     "dsa_ceiling_mfma": (ctypes.c_int, [_I, _I, _I, _P, _P, _P]),
     "dsa_ceiling_read": (ctypes.c_int, [_P, _Z, _I, _P, _P]),
 }
@@ -259,8 +261,42 @@ def sparse_mqa_decode(q, kv_cache, page_table, ctx_lens, idx, d_v: int, scale: f
     return out, lse
 
 
+def sparse_mqa_decode_noalloc(q, kv_cache, page_table, ctx_lens, idx, d_v: int, scale: float,
+                              n_split: int = 0, out=None, lse=None, want_lse: bool = True):
+    """dsa_sparse_mqa_decode_noalloc: as sparse_mqa_decode, with the split partials in the
+    library's static per-device scratch array instead of a workspace (outputs are still
+    allocated here unless given)."""
+    lib = load_library()
+    _need(q, "q", _BF16, 3)
+    dev = q.device
+    _need(kv_cache, "kv_cache", _BF16, 3, dev)
+    _need(page_table, "page_table", _I32, 2, dev)
+    _need(ctx_lens, "ctx_lens", _I32, 1, dev)
+    _need(idx, "idx", _I32, 2, dev)
+    B, H, D_k = q.shape
+    n_pages, page_size, dk = kv_cache.shape
+    top_k = idx.shape[1]
+    if dk != D_k or page_table.shape[0] != B or ctx_lens.shape[0] != B or idx.shape[0] != B:
+        raise ValueError("inconsistent decode shapes")
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", _BF16, 3, dev, shape=(B, H, d_v))
+    if lse is not None:
+        _need(lse, "lse", _F32, 2, dev, shape=(B, H))
+    _check(lib.dsa_sparse_mqa_decode_noalloc(_ptr(q), _ptr(kv_cache), _ptr(page_table),
+                                             _ptr(ctx_lens), _ptr(idx), B, page_table.shape[1],
+                                             n_pages, page_size, H, D_k, d_v, top_k,
+                                             float(scale), n_split, _ptr(out), _ptr(lse),
+                                             _stream(dev)),
+           "dsa_sparse_mqa_decode_noalloc")
+    return out, lse
+
+
 __all__ = ["load_library", "DSAError", "indexer_topk", "indexer_topk_paged",
-           "sparse_mqa_prefill", "sparse_mqa_decode", "indexer_topk_workspace_size",
+           "sparse_mqa_prefill", "sparse_mqa_decode", "sparse_mqa_decode_noalloc",
+           "indexer_topk_workspace_size",
            "indexer_topk_paged_workspace_size", "sparse_mqa_decode_workspace_size",
            "SIGNATURES", "LIB_PATH"]
 

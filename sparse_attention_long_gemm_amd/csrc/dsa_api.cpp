@@ -58,6 +58,9 @@ const char* dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED_SHAPE: return "DSA_ERR_UNSUPPORTED_SHAPE: no kernel for this shape";
     case DSA_ERR_WORKSPACE_TOO_SMALL: return "DSA_ERR_WORKSPACE_TOO_SMALL: workspace too small";
     case DSA_ERR_HIP: return "DSA_ERR_HIP: kernel launch failed";
+    case DSA_ERR_SCRATCH_LIMIT:
+      return "DSA_ERR_SCRATCH_LIMIT: the call needs more scratch than the allocation-free entry "
+             "point holds (DSA_NOALLOC_SCRATCH_BYTES); use the workspace variant";
     default: return "unknown dsa_status";
   }
 }
@@ -131,6 +134,52 @@ size_t dsa_sparse_mqa_decode_workspace_size(int32_t B, int32_t H, int32_t D_v, i
   return (size_t)B * ns * H * ((size_t)D_v * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode-attention entry points; fills the launch arguments except
+// the partials.  *done is set when there is nothing to launch (B == 0).
+dsa_status decode_args(const uint16_t* q, const uint16_t* kv_cache, const int32_t* page_table,
+                       const int32_t* ctx_lens, const int32_t* idx, int32_t B,
+                       int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t H,
+                       int32_t D_k, int32_t D_v, int32_t top_k, float scale, int32_t n_split,
+                       uint16_t* out, float* lse, dsa::MqaArgs* a, bool* done) {
+  *done = false;
+  if (B < 0 || !paging_ok(max_pages, n_pages, page_size) || !isfinite(scale) || n_split < 0 ||
+      n_split > kMaxSplit)
+    return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > kMaxH || !dsa::mqa_shape_supported(D_k, D_v) || top_k < 1 ||
+      top_k > kMaxTopK)
+    return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (B == 0) {
+    *done = true;
+    return DSA_OK;
+  }
+  if (B > 65535 * 16) return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (!q || !kv_cache || !page_table || !ctx_lens || !idx || !out) return DSA_ERR_INVALID_ARG;
+  int ns, rps;
+  decode_split(B, top_k, n_split, &ns, &rps);
+  *a = dsa::MqaArgs{};
+  a->q = q; a->kv = kv_cache; a->idx = idx; a->qpos_or_ctx = ctx_lens;
+  a->page_table = page_table; a->max_pages = max_pages; a->n_pages = n_pages;
+  a->page_size = page_size; a->n_kv = 0; a->n_q = B; a->H = H; a->D_k = D_k; a->D_v = D_v;
+  a->top_k = top_k; a->scale = scale; a->n_split = ns; a->rows_per_split = rps; a->out = out;
+  a->lse = lse;
+  return DSA_OK;
+}
+
+void set_partials(dsa::MqaArgs* a, void* base) {
+  if (a->n_split > 1) {
+    a->part_o = reinterpret_cast<uint16_t*>(base);
+    a->part_ml = reinterpret_cast<float*>(a->part_o + (size_t)a->n_q * a->n_split * a->H * a->D_v);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
 dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
                                  const int32_t* page_table, const int32_t* ctx_lens,
                                  const int32_t* idx, int32_t B, int32_t max_pages,
@@ -138,27 +187,36 @@ dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
                                  int32_t D_v, int32_t top_k, float scale, int32_t n_split,
                                  uint16_t* out, float* lse, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || !paging_ok(max_pages, n_pages, page_size) || !isfinite(scale) || n_split < 0 ||
-      n_split > kMaxSplit)
-    return DSA_ERR_INVALID_ARG;
-  if (H < 1 || H > kMaxH || !dsa::mqa_shape_supported(D_k, D_v) || top_k < 1 ||
-      top_k > kMaxTopK)
-    return DSA_ERR_UNSUPPORTED_SHAPE;
-  if (B == 0) return DSA_OK;
-  if (B > 65535 * 16) return DSA_ERR_UNSUPPORTED_SHAPE;
-  if (!q || !kv_cache || !page_table || !ctx_lens || !idx || !out) return DSA_ERR_INVALID_ARG;
-  int ns, rps;
-  decode_split(B, top_k, n_split, &ns, &rps);
+  dsa::MqaArgs a;
+  bool done;
+  dsa_status st = decode_args(q, kv_cache, page_table, ctx_lens, idx, B, max_pages, n_pages,
+                              page_size, H, D_k, D_v, top_k, scale, n_split, out, lse, &a, &done);
+  if (st != DSA_OK || done) return st;
   const size_t need = dsa_sparse_mqa_decode_workspace_size(B, H, D_v, top_k, n_split);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  dsa::MqaArgs a{};
-  a.q = q; a.kv = kv_cache; a.idx = idx; a.qpos_or_ctx = ctx_lens; a.page_table = page_table;
-  a.max_pages = max_pages; a.n_pages = n_pages; a.page_size = page_size; a.n_kv = 0;
-  a.n_q = B; a.H = H; a.D_k = D_k; a.D_v = D_v; a.top_k = top_k; a.scale = scale;
-  a.n_split = ns; a.rows_per_split = rps; a.out = out; a.lse = lse;
-  if (ns > 1) {
-    a.part_o = reinterpret_cast<uint16_t*>(workspace);
-    a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)B * ns * H * D_v);
+  set_partials(&a, workspace);
+  return from_hip(dsa::launch_sparse_mqa(a, stream));
+}
+
+dsa_status dsa_sparse_mqa_decode_noalloc(const uint16_t* q, const uint16_t* kv_cache,
+                                         const int32_t* page_table, const int32_t* ctx_lens,
+                                         const int32_t* idx, int32_t B, int32_t max_pages,
+                                         int32_t n_pages, int32_t page_size, int32_t H,
+                                         int32_t D_k, int32_t D_v, int32_t top_k, float scale,
+                                         int32_t n_split, uint16_t* out, float* lse,
+                                         hipStream_t stream) {
+  static_assert(DSA_NOALLOC_SCRATCH_BYTES == dsa::kNoAllocScratchBytes, "scratch size");
+  dsa::MqaArgs a;
+  bool done;
+  dsa_status st = decode_args(q, kv_cache, page_table, ctx_lens, idx, B, max_pages, n_pages,
+                              page_size, H, D_k, D_v, top_k, scale, n_split, out, lse, &a, &done);
+  if (st != DSA_OK || done) return st;
+  const size_t need = dsa_sparse_mqa_decode_workspace_size(B, H, D_v, top_k, n_split);
+  if (need > dsa::kNoAllocScratchBytes) return DSA_ERR_SCRATCH_LIMIT;
+  if (need > 0) {
+    void* base = nullptr;
+    if (dsa::noalloc_scratch(&base) != hipSuccess) return DSA_ERR_HIP;
+    set_partials(&a, base);
   }
   return from_hip(dsa::launch_sparse_mqa(a, stream));
 }

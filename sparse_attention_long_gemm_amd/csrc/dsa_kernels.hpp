@@ -40,4 +40,9 @@ struct MqaArgs {
 bool mqa_shape_supported(int D_k, int D_v);
 hipError_t launch_sparse_mqa(const MqaArgs& a, hipStream_t stream);
 
+// Bytes of the per-device static scratch array of the allocation-free decode entry point.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of the current GPU's scratch array (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace dsa

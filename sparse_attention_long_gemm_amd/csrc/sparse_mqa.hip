@@ -30,6 +30,7 @@
 #include "dsa_common.hpp"
 #include "dsa_kernels.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace dsa {
@@ -554,6 +555,37 @@ hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------------------------------
+// Allocation-free decode: the split partials live in a static device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy (kNoAllocScratchBytes) until the
+// process ends.  Host code never uses the array's name as an address: the device address of
+// each GPU's copy is looked up once, with that GPU current, on the first call there.
+// ------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool mqa_shape_supported(int D_k, int D_v) {
   return (D_k == 576 && D_v == 512) || (D_k == 64 && D_v == 64) || (D_k == 96 && D_v == 64);

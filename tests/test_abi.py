@@ -24,7 +24,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("dsa_indexer_topk", "dsa_indexer_topk_paged", "dsa_sparse_mqa_prefill",
-              "dsa_sparse_mqa_decode", "dsa_status_string", "dsa_abi_version"):
+              "dsa_sparse_mqa_decode", "dsa_sparse_mqa_decode_noalloc", "dsa_status_string",
+              "dsa_abi_version"):
         assert n in names
 
 
@@ -41,7 +42,7 @@ def test_abi_version_and_status_strings():
     assert lib.dsa_abi_version() == 1
     for code, name in [(0, b"DSA_OK"), (-1, b"DSA_ERR_INVALID_ARG"),
                        (-2, b"DSA_ERR_UNSUPPORTED_SHAPE"), (-3, b"DSA_ERR_WORKSPACE_TOO_SMALL"),
-                       (-4, b"DSA_ERR_HIP")]:
+                       (-4, b"DSA_ERR_HIP"), (-5, b"DSA_ERR_SCRATCH_LIMIT")]:
         assert lib.dsa_status_string(code).startswith(name)
     assert lib.dsa_status_string(12345) == b"unknown dsa_status"
 
@@ -137,6 +138,23 @@ def test_mqa_host_checks():
         a = list(ok)
         a[pos] = val
         assert g(*a) == code, (pos, val)
+
+
+@host_only
+def test_noalloc_decode_host_checks():
+    """The allocation-free decode applies the workspace variant's checks, and refuses a call
+    whose partials exceed its static scratch array, before anything is launched."""
+    g = dsa.load_library().dsa_sparse_mqa_decode_noalloc
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2048, 70000, 64, 128, 576, 512, 2048, 0.04, 0,
+          FAKE, None, None]
+    for change, code in [({13: float("nan")}, -1), ({14: 17}, -1), ({8: 0}, -1),
+                         ({2: None}, -1), ({10: 100}, -2), ({9: 129}, -2),
+                         ({5: 600, 14: 4}, -5),   # 600 x 4 splits x 128 heads x 1032 B > 64 MiB
+                         ({5: 0}, 0)]:            # nothing to do
+        a = list(ok)
+        for pos, val in change.items():
+            a[pos] = val
+        assert g(*a) == code, change
 
 
 def test_binding_rejects_host_tensors():
