@@ -73,9 +73,17 @@ const char* dsa_status_string(int status);
  *                                with t clamped to n_keys-1; a negative t selects nothing
  * out_idx [n_q, top_k]     int32 selection, ascending positions then -1 (see above)
  *
- * Scores are computed in fp32 from exact FP8 products; the n_q x n_keys score matrix is
- * never stored: each workgroup streams key tiles and keeps a per-row candidate list in the
- * workspace.  Selection is exact under (score desc, position asc), with -0 == +0.
+ * The n_q x n_keys score matrix is never stored: each workgroup streams key tiles and keeps
+ * a per-row candidate list in the workspace.  The selection is the exact top_k of the scores
+ * as computed, under (score desc, position asc), with -0 == +0.
+ * Precision: scores are computed in fp32 from exact FP8 products, with ReLU applied as
+ * w ReLU(x) = (w x + w |x|) / 2 (the |x| half by fma per head, the linear half as one product
+ * with the weighted query sum).  When every product sum and weighted partial sum is exact in
+ * fp32 (FP8 operands on a dyadic grid with power-of-two weights: the tested workloads) the
+ * computed scores equal the definition's and the selection is bit-exact.  Otherwise each
+ * computed score is within 2^-16 * M of the exact one, M = sum_j |w[t,j]| sum_i
+ * |q_I[t,j,i]| |k_I[s,i]|; a key whose heads are all <= 0 scores within that bound of 0 rather
+ * than exactly 0, so the order among such keys need not follow their positions.
  * ------------------------------------------------------------------------------------- */
 size_t dsa_indexer_topk_workspace_size(int32_t n_q, int32_t top_k);
 
@@ -99,6 +107,12 @@ dsa_status dsa_indexer_topk(const uint8_t* q_idx, const float* w, const uint8_t*
  * ctx_lens   [B]                         int32 context length (>= 0, <= max_pages*page_size);
  *                                              candidates are s in [0, ctx)
  * out_idx    [B, top_k]                  int32 logical positions, ascending, then -1
+ *
+ * Scores are sum_j w_j max(x_j, 0) accumulated by fma in fp32 from the exact FP8 products: a
+ * key whose heads are all <= 0 scores exactly 0; otherwise the same 2^-16 * M bound as the
+ * prefill indexer holds, and on a dyadic grid with power-of-two weights the selection is
+ * bit-exact.  The selection is the exact top_k of the computed scores (score desc, position
+ * asc).
  * ------------------------------------------------------------------------------------- */
 size_t dsa_indexer_topk_paged_workspace_size(int32_t B, int32_t max_pages, int32_t page_size);
 
