@@ -162,6 +162,37 @@ dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
                                  size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Cache write: append new tokens to the paged caches the decode calls read.  Defines the step
+ * just before the paged indexer and attention: the indexer keeps its keys in FP8 (jdon.com
+ * "DeepSeek-V3.2-Exp" article, paragraph on the lightning indexer) in 64-token pages
+ * (mundobytes.com page, sections "Quick guide to running locally" and "Open kernels and
+ * ecosystem support"), next to the shared latent KV rows (openi.cn page, MLA/MQA item).
+ *
+ * k_new      [T, d_I]                   bf16  indexer keys of the new tokens, or NULL
+ * kv_new     [T, D_k]                   bf16  latent KV rows of the new tokens, or NULL
+ * seq        [T]                        int32 sequence of row r (page-table row), or NULL:
+ *                                             row r belongs to sequence r
+ * pos        [T]                        int32 logical position of row r in its sequence
+ * page_table [B, max_pages]             int32 as in dsa_indexer_topk_paged
+ * k_cache    [n_pages, page_size, d_I]  FP8   written at the rows' slots (if k_new)
+ * kv_cache   [n_pages, page_size, D_k]  bf16  written at the rows' slots (if kv_new)
+ *
+ * Row r goes to page page_table[seq[r]*max_pages + pos[r]/page_size], slot pos[r] % page_size;
+ * a row whose position is negative, whose page index is >= max_pages or whose page-table
+ * entry is outside [0, n_pages) writes nothing.  The k_I values are quantised to e4m3fn by
+ * rounding to nearest (ties to the even code), saturating finite values and infinities at
+ * +-448, NaN to NaN; the KV rows are copied bit for bit.  Two rows with the same slot in one
+ * call race (either may win).  Nothing else in the caches is touched.
+ * Requires d_I a multiple of 16 (<= 128) and D_k a multiple of 8 (<= 1024), 16-byte aligned
+ * rows in k_new / kv_new and 8-byte aligned caches.
+ * ------------------------------------------------------------------------------------- */
+dsa_status dsa_cache_append(const uint16_t* k_new, const uint16_t* kv_new, const int32_t* seq,
+                            const int32_t* pos, const int32_t* page_table, int32_t T,
+                            int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t d_I,
+                            int32_t D_k, uint8_t* k_cache, uint16_t* kv_cache,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Allocation-free variant of dsa_sparse_mqa_decode, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  *

@@ -26,6 +26,23 @@ def e4m3fn_value(code: int) -> Fraction:
     return -mag if s else mag
 
 
+def nearest_e4m3fn(x: Fraction) -> int:
+    """Saturating round-to-nearest e4m3fn code of an exact value, by trying every code: the
+    finite code at the smallest exact distance, a tie going to the even code, magnitudes at or
+    past 448 to the largest finite code; the sign is carried over (also for zero results)."""
+    neg = x < 0
+    a = -x if neg else x
+    if a >= 448:
+        best = 0x7E
+    else:
+        best, best_d = None, None
+        for code in range(0x7F):                  # 0x00 .. 0x7e: every finite magnitude
+            d = abs(e4m3fn_value(code) - a)
+            if best_d is None or d < best_d or (d == best_d and code % 2 == 0):
+                best, best_d = code, d
+    return best | (0x80 if neg else 0)
+
+
 def bf16_value(bits: int) -> float:
     """bf16 bit pattern (uint16) -> float, by building the fp32 pattern bits << 16."""
     import struct

@@ -270,6 +270,75 @@ def decode(inp: dict, seqs=None, idx=None):
 
 
 # ----------------------------------------------------------------------------------------
+# Cache write: FP8 quantisation of new indexer keys and the paged append
+# ----------------------------------------------------------------------------------------
+
+
+def quantize_e4m3fn(x) -> np.ndarray:
+    """Nearest e4m3fn code of each value (uint8), from the format's value set.
+
+    The indexer keeps its keys in FP8 (jdon.com article, lightning-indexer paragraph).  Reading
+    (the pages give no conversion rule): round to the nearest representable value, a tie going
+    to the even code (the codes of two neighbouring values differ by one); finite values and
+    infinities past the largest magnitude, 448, saturate to +-448; NaN gives the NaN code 0x7f
+    with the sign bit of the input; the sign of zero is kept.
+    """
+    v = np.asarray(x, dtype=np.float64)
+    finite = E4M3FN[:127]                        # codes 0x00..0x7e: 0 .. 448, increasing
+    out = np.empty(v.shape, dtype=np.uint8)
+    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
+    for i, val in enumerate(flat_v):
+        neg = np.signbit(val)
+        a = abs(val)
+        if np.isnan(val):
+            code = 0x7F
+        elif a >= 448.0:
+            code = 0x7E
+        else:
+            hi = int(np.searchsorted(finite, a, side="left"))   # finite[hi] >= a
+            if finite[hi] == a:
+                code = hi
+            else:
+                lo = hi - 1
+                d_lo, d_hi = a - finite[lo], finite[hi] - a
+                code = lo if d_lo < d_hi else hi if d_hi < d_lo else (lo if lo % 2 == 0 else hi)
+        flat_o[i] = code | (0x80 if neg else 0)
+    return out
+
+
+def cache_append(k_cache, kv_cache, page_table, seq, pos, k_new, kv_new):
+    """The caches after writing the new rows: row r of sequence seq[r] (r if seq is None) at
+    logical position pos[r] goes to page page_table[seq[r], pos[r] // P], slot pos[r] % P, its
+    k_I quantised to e4m3fn and its KV row copied; a row with a negative position, a page index
+    past the table or a page-table entry outside [0, n_pages) writes nothing.  Returns new host
+    arrays (FP8 codes, bf16 as bits); either cache may be None when its rows are not given.
+    (mundobytes.com page, "Quick guide to running locally": 64-token pages.)
+    """
+    pt = _np(page_table).astype(np.int64)
+    pos = _np(pos).astype(np.int64)
+    T = pos.shape[0]
+    seq = np.arange(T) if seq is None else _np(seq).astype(np.int64)
+    kc = None if k_cache is None else _np(k_cache).copy()
+    kvc = None if kv_cache is None else _np(kv_cache).copy()
+    geo = (kc if kc is not None else kvc).shape
+    n_pages, P = geo[0], geo[1]
+    kq = None if k_new is None else quantize_e4m3fn(decode_bf16(k_new))
+    kvb = None if kv_new is None else _np(kv_new)
+    for r in range(T):
+        b, p = int(seq[r]), int(pos[r])
+        if b < 0 or p < 0 or p // P >= pt.shape[1]:
+            continue
+        page = int(pt[b, p // P])
+        if page < 0 or page >= n_pages:
+            continue
+        if kq is not None:
+            kc[page, p % P] = kq[r]
+        if kvb is not None:
+            kvc[page, p % P] = kvb[r]
+    return kc, kvc
+
+
+# ----------------------------------------------------------------------------------------
 # Work model used to extrapolate sampled oracle timings
 # ----------------------------------------------------------------------------------------
 
@@ -291,6 +360,7 @@ def selected_pairs(L: int, k: int) -> int:
 
 __all__ = [
     "E4M3FN", "decode_e4m3fn", "decode_bf16", "indexer_scores", "topk_select", "sparse_mqa",
-    "valid_selected", "prefill_indexer_topk", "prefill", "paged_gather", "paged_rows", "decode", "row_work",
+    "valid_selected", "prefill_indexer_topk", "prefill", "paged_gather", "paged_rows", "decode",
+    "quantize_e4m3fn", "cache_append", "row_work",
     "causal_pairs", "selected_pairs",
 ]

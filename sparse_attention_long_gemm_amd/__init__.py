@@ -42,6 +42,7 @@ SIGNATURES = {
     "dsa_sparse_mqa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "dsa_sparse_mqa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                              _F, _I, _P, _P, _P, _Z, _P]),
+    "dsa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dsa_sparse_mqa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                      _I, _I, _I, _F, _I, _P, _P, _P]),
     "dsa_ceiling_mfma": (ctypes.c_int, [_I, _I, _I, _P, _P, _P]),
@@ -261,6 +262,52 @@ def sparse_mqa_decode(q, kv_cache, page_table, ctx_lens, idx, d_v: int, scale: f
     return out, lse
 
 
+def cache_append(page_table, pos, k_cache=None, kv_cache=None, k_new=None, kv_new=None,
+                 seq=None):
+    """Append new tokens to the paged caches (dsa_cache_append): k_new [T, d_I] bf16 is
+    quantised to e4m3fn into k_cache [n_pages, page_size, d_I] (uint8 / float8_e4m3fn) and
+    kv_new [T, D_k] bf16 copied into kv_cache [n_pages, page_size, D_k] at logical position
+    pos[r] of sequence seq[r] (default: r).  The caches are updated in place."""
+    lib = load_library()
+    _need(page_table, "page_table", _I32, 2)
+    dev = page_table.device
+    _need(pos, "pos", _I32, 1, dev)
+    T = pos.shape[0]
+    if seq is not None:
+        _need(seq, "seq", _I32, 1, dev, shape=(T,))
+    if k_new is None and kv_new is None:
+        raise ValueError("nothing to append: give k_new and/or kv_new")
+    d_I = D_k = 0
+    geo = None
+    if k_new is not None:
+        _need(k_new, "k_new", _BF16, 2, dev)
+        d_I = k_new.shape[1]
+        _need(k_new, "k_new", _BF16, 2, dev, shape=(T, d_I))
+        if k_cache is None:
+            raise ValueError("k_new given without k_cache")
+        _need(k_cache, "k_cache", _FP8, 3, dev)
+        if k_cache.shape[2] != d_I:
+            raise ValueError("k_cache rows do not match k_new")
+        geo = tuple(k_cache.shape[:2])
+    if kv_new is not None:
+        _need(kv_new, "kv_new", _BF16, 2, dev)
+        D_k = kv_new.shape[1]
+        _need(kv_new, "kv_new", _BF16, 2, dev, shape=(T, D_k))
+        if kv_cache is None:
+            raise ValueError("kv_new given without kv_cache")
+        _need(kv_cache, "kv_cache", _BF16, 3, dev)
+        if kv_cache.shape[2] != D_k or (geo is not None and tuple(kv_cache.shape[:2]) != geo):
+            raise ValueError("kv_cache does not match kv_new or k_cache")
+        geo = tuple(kv_cache.shape[:2])
+    n_pages, page_size = geo
+    _check(lib.dsa_cache_append(_ptr(k_new), _ptr(kv_new), _ptr(seq), _ptr(pos),
+                                _ptr(page_table), T, page_table.shape[1], n_pages, page_size,
+                                d_I, D_k, _ptr(k_cache if k_new is not None else None),
+                                _ptr(kv_cache if kv_new is not None else None), _stream(dev)),
+           "dsa_cache_append")
+    return k_cache, kv_cache
+
+
 def sparse_mqa_decode_noalloc(q, kv_cache, page_table, ctx_lens, idx, d_v: int, scale: float,
                               n_split: int = 0, out=None, lse=None, want_lse: bool = True):
     """dsa_sparse_mqa_decode_noalloc: as sparse_mqa_decode, with the split partials in the
@@ -295,7 +342,7 @@ def sparse_mqa_decode_noalloc(q, kv_cache, page_table, ctx_lens, idx, d_v: int, 
 
 
 __all__ = ["load_library", "DSAError", "indexer_topk", "indexer_topk_paged",
-           "sparse_mqa_prefill", "sparse_mqa_decode", "sparse_mqa_decode_noalloc",
+           "sparse_mqa_prefill", "sparse_mqa_decode", "sparse_mqa_decode_noalloc", "cache_append",
            "indexer_topk_workspace_size",
            "indexer_topk_paged_workspace_size", "sparse_mqa_decode_workspace_size",
            "SIGNATURES", "LIB_PATH"]

@@ -124,6 +124,25 @@ dsa_status dsa_sparse_mqa_prefill(const uint16_t* q, const uint16_t* kv, int32_t
   return from_hip(dsa::launch_sparse_mqa(a, stream));
 }
 
+dsa_status dsa_cache_append(const uint16_t* k_new, const uint16_t* kv_new, const int32_t* seq,
+                            const int32_t* pos, const int32_t* page_table, int32_t T,
+                            int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t d_I,
+                            int32_t D_k, uint8_t* k_cache, uint16_t* kv_cache,
+                            hipStream_t stream) {
+  if (T < 0 || !paging_ok(max_pages, n_pages, page_size)) return DSA_ERR_INVALID_ARG;
+  if (k_new != nullptr && (d_I < 16 || d_I > kMaxDI || d_I % 16 != 0))
+    return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (kv_new != nullptr && (D_k < 8 || D_k > 1024 || D_k % 8 != 0))
+    return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return DSA_OK;
+  if (T > 0x7fffffff / 2 || (!k_new && !kv_new) || !pos || !page_table ||
+      (k_new && !k_cache) || (kv_new && !kv_cache))
+    return DSA_ERR_INVALID_ARG;
+  return from_hip(dsa::launch_cache_append(k_new, kv_new, seq, pos, page_table, T, max_pages,
+                                           n_pages, page_size, d_I, D_k, k_cache, kv_cache,
+                                           stream));
+}
+
 size_t dsa_sparse_mqa_decode_workspace_size(int32_t B, int32_t H, int32_t D_v, int32_t top_k,
                                             int32_t n_split) {
   if (B < 0 || H < 1 || D_v < 1 || top_k < 1 || top_k > kMaxTopK || n_split < 0) return 0;

@@ -20,6 +20,12 @@ hipError_t launch_indexer_topk_paged(const uint8_t* q_idx, const float* w, const
                                      int max_pages, int n_pages, int page_size, int H_I, int d_I,
                                      int top_k, int32_t* out_idx, void* ws, hipStream_t stream);
 
+// cache_write.hip
+hipError_t launch_cache_append(const uint16_t* k_new, const uint16_t* kv_new, const int32_t* seq,
+                               const int32_t* pos, const int32_t* page_table, int T,
+                               int max_pages, int n_pages, int page_size, int d_I, int D_k,
+                               uint8_t* k_cache, uint16_t* kv_cache, hipStream_t stream);
+
 // sparse_mqa.hip
 struct MqaArgs {
   const uint16_t* q;

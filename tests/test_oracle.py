@@ -300,6 +300,75 @@ def test_decode_invariant_under_page_permutation():
     assert np.array_equal(idx, i2) and np.array_equal(o, o2) and np.array_equal(lse, l2)
 
 
+# --------------------------------------------------------------------------- cache write
+
+def _all_bf16():
+    return torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+
+
+def test_quantize_e4m3fn_matches_torch_cast_on_every_bf16_value():
+    """Every bf16 bit pattern: the saturating quantiser equals torch's (round-to-nearest-even)
+    e4m3fn cast of the value clamped to [-448, 448]; NaNs give the NaN code with their sign."""
+    allb = _all_bf16()
+    v = allb.double().numpy()
+    q = orc.quantize_e4m3fn(v)
+    fin = ~np.isnan(v)
+    ref = allb.float().clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q[fin], ref[fin])
+    assert set(np.unique(q[~fin]).tolist()) == {0x7F, 0xFF}
+    assert orc.quantize_e4m3fn(np.array([-0.0]))[0] == 0x80
+    assert orc.quantize_e4m3fn(np.array([np.inf, -np.inf, 1e30])).tolist() == [0x7E, 0xFE, 0x7E]
+
+
+def test_quantize_e4m3fn_equals_exact_nearest_brute_force():
+    """Against the exact-distance search over all codes (Fractions): every midpoint between
+    neighbouring codes (the ties), points just off them, and a spread of bf16 values."""
+    from fractions import Fraction
+    vals = [brute.e4m3fn_value(c) for c in range(0x7F)]
+    pts = []
+    for a, b in zip(vals, vals[1:]):
+        mid = (a + b) / 2
+        pts += [mid, mid + Fraction(1, 2 ** 20), mid - Fraction(1, 2 ** 20)]
+    g = torch.Generator().manual_seed(3)
+    pick = torch.randint(0, 65536, (600,), generator=g)
+    for b in _all_bf16()[pick].double().numpy():
+        if np.isfinite(b):
+            pts.append(Fraction(float(b)))
+    pts += [-p for p in pts[:50]] + [Fraction(448), Fraction(470), Fraction(480), Fraction(10 ** 6)]
+    got = orc.quantize_e4m3fn(np.array([float(p) for p in pts]))
+    want = [brute.nearest_e4m3fn(p) for p in pts]
+    assert got.tolist() == want
+
+
+def test_cache_append_writes_the_slots_and_nothing_else():
+    """The appended rows come back through the page table as the quantised keys and the exact
+    KV rows; every other byte is unchanged; rows with an invalid slot write nothing; the result
+    equals a scatter written with torch's indexing (a library data move)."""
+    g = torch.Generator().manual_seed(7)
+    P, n_pages, d_I, D_k = 8, 12, 16, 24
+    kc = torch.randint(0, 256, (n_pages, P, d_I), generator=g, dtype=torch.int32).to(torch.uint8)
+    kvc = torch.randn((n_pages, P, D_k), generator=g).to(torch.bfloat16)
+    pt = torch.tensor([[3, 7, 1, -1], [0, 11, 5, 40]], dtype=torch.int32)
+    seq = torch.tensor([0, 1, 0, 1, 1, 0, 1], dtype=torch.int32)
+    pos = torch.tensor([0, 9, 20, 23, 31, -2, 25], dtype=torch.int32)   # last three invalid
+    T = pos.shape[0]
+    k_new = (torch.randn((T, d_I), generator=g) * 3).to(torch.bfloat16)
+    kv_new = torch.randn((T, D_k), generator=g).to(torch.bfloat16)
+    kc2, kvc2 = orc.cache_append(kc, kvc, pt, seq, pos, k_new, kv_new)
+    ref_k, ref_kv = kc.clone(), kvc.clone()
+    q = orc.quantize_e4m3fn(orc.decode_bf16(k_new))
+    for r in range(4):
+        b, p = int(seq[r]), int(pos[r])
+        page = int(pt[b, p // P])
+        ref_k[page, p % P] = torch.from_numpy(q[r])
+        ref_kv[page, p % P] = kv_new[r]
+        assert np.array_equal(orc.paged_gather(kc2, pt[b], [p], P)[0], q[r])
+    assert np.array_equal(kc2, ref_k.numpy())
+    assert np.array_equal(kvc2, ref_kv.view(torch.int16).numpy())
+    assert np.array_equal(orc.decode_e4m3fn(q), orc.decode_e4m3fn(
+        k_new.float().clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)))
+
+
 # --------------------------------------------------------------------------- generators
 
 def test_generators_are_seeded_and_on_grid():
@@ -335,6 +404,7 @@ def _pins_pass(monkeypatched):
         test_attention_handworked_example()
         test_full_selection_equals_dense_causal_sdpa(96, 64)
         test_decode_equals_prefill_last_row()
+        test_quantize_e4m3fn_matches_torch_cast_on_every_bf16_value()
     except AssertionError:
         return False
     return True
@@ -370,7 +440,24 @@ def _wrong_valid_off_by_one(idx_row, t):
     return idx_row[(idx_row >= 0) & (idx_row < t)]
 
 
+def _wrong_quantize_ties_away(x):
+    v = np.asarray(x, dtype=np.float64)
+    finite = orc.E4M3FN[:127]
+    out = np.empty(v.shape, dtype=np.uint8)
+    for i, val in enumerate(v.reshape(-1)):
+        a = min(abs(val), 448.0) if not np.isnan(val) else val
+        if np.isnan(a):
+            code = 0x7F
+        else:
+            hi = int(np.searchsorted(finite, a))
+            lo = max(hi - 1, 0)
+            code = hi if (finite[hi] - a) <= (a - finite[lo]) else lo
+        out.reshape(-1)[i] = code | (0x80 if np.signbit(val) else 0)
+    return out
+
+
 @pytest.mark.parametrize("name,attr,bad", [
+    ("FP8 ties rounded away from zero", "quantize_e4m3fn", _wrong_quantize_ties_away),
     ("tie-break to highest index", "topk_select", _wrong_topk_high_index),
     ("ReLU dropped", "indexer_scores", _wrong_scores_no_relu),
     ("head weights dropped", "indexer_scores", _wrong_scores_no_weight),
