@@ -219,6 +219,82 @@ def decode_inputs(sp: DecodeSpec, device="cpu", seed: int | None = None, ctx_len
     return d
 
 
+@dataclass
+class BatchedSpec:
+    """Many sequences in paged caches, prefilled in one call: sequence b holds seq_lens[b]
+    tokens, of which positions q_start[b] .. seq_lens[b]-1 are queried (q_start > 0: a chunk
+    against a cached prefix)."""
+    seq_lens: tuple = (1000, 3000)
+    q_start: tuple | None = None
+    page_size: int = 64
+    idx: IndexerSpec = field(default_factory=IndexerSpec)
+    mqa: MqaSpec | None = field(default_factory=MqaSpec)
+    spare_pages: int = 0
+    seed: int = 0
+
+
+def batched_inputs(sp: BatchedSpec, device="cpu", seed: int | None = None, row_order=None):
+    """Inputs of a batched prefill over paged caches.
+
+    The keys and KV rows of all sequences are drawn as one contiguous run of rows
+    (``k_flat`` / ``kv_flat``, sequence b at rows seq_off[b] ..), then laid into pages of a
+    random permutation of the pool (one page table for both caches).  Query rows are listed
+    sequence by sequence (``q_seq`` non-decreasing) unless ``row_order`` permutes them.
+    """
+    seed = sp.seed if seed is None else seed
+    P, ix, m = sp.page_size, sp.idx, sp.mqa
+    lens = [int(x) for x in sp.seq_lens]
+    starts = [0] * len(lens) if sp.q_start is None else [int(x) for x in sp.q_start]
+    B = len(lens)
+    off = [0]
+    for n in lens:
+        off.append(off[-1] + n)
+    total = off[-1]
+    pages_per = [(n + P - 1) // P for n in lens]
+    n_pages = sum(pages_per) + sp.spare_pages
+    max_pages = max(pages_per)
+    g = _gen(seed, _T_PERM, "cpu")
+    perm = torch.randperm(n_pages, generator=g).to(torch.int32)
+    pt = torch.full((B, max_pages), -1, dtype=torch.int32)
+    o = 0
+    for b, npg in enumerate(pages_per):
+        pt[b, :npg] = perm[o:o + npg]
+        o += npg
+    k_flat = grid_fp8((total, ix.d_I), ix.grid_lo, ix.grid_hi, ix.grid_step, seed, _T_KIDX, device)
+    k_cache = torch.zeros((n_pages, P, ix.d_I), dtype=torch.uint8, device=device)
+    kv_flat = kv_cache = None
+    if m is not None:
+        kv_flat = normal_bf16((total, m.D_k), m.sigma, seed, _T_KV, device)
+        kv_cache = torch.zeros((n_pages, P, m.D_k), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        contiguous_to_pages(k_flat[off[b]:off[b + 1]], pt, b, n_pages, P, k_cache)
+        if m is not None:
+            contiguous_to_pages(kv_flat[off[b]:off[b + 1]], pt, b, n_pages, P, kv_cache)
+    q_seq = torch.cat([torch.full((lens[b] - starts[b],), b, dtype=torch.int32) for b in range(B)])
+    q_pos = torch.cat([torch.arange(starts[b], lens[b], dtype=torch.int32) for b in range(B)])
+    # query-side draws are made for every token of every sequence, then the queried rows taken
+    flat_rows = torch.cat([torch.arange(off[b] + starts[b], off[b + 1]) for b in range(B)])
+    if row_order is not None:
+        ro = torch.as_tensor(row_order, dtype=torch.int64)
+        q_seq, q_pos, flat_rows = q_seq[ro], q_pos[ro], flat_rows[ro]
+    fr = flat_rows.to(device)
+    d = {
+        "seq_lens": lens, "q_start": starts, "seq_off": off,
+        "page_table": pt.to(device), "page_size": P, "n_pages": n_pages, "max_pages": max_pages,
+        "k_flat": k_flat, "k_cache": k_cache,
+        "q_seq": q_seq.to(device), "q_pos": q_pos.to(device),
+        "q_idx": grid_fp8((total, ix.H_I, ix.d_I), ix.grid_lo, ix.grid_hi, ix.grid_step, seed,
+                          _T_QIDX, device)[fr].contiguous(),
+        "w": choice_f32((total, ix.H_I), ix.w_choices, seed, _T_W, device)[fr].contiguous(),
+        "top_k": ix.top_k,
+    }
+    if m is not None:
+        d["kv_flat"], d["kv_cache"] = kv_flat, kv_cache
+        d["q"] = normal_bf16((total, m.H, m.D_k), m.sigma, seed, _T_Q, device)[fr].contiguous()
+        d["D_v"], d["scale"] = m.D_v, m.scale
+    return d
+
+
 def identity_page_table(ctx_lens, page_size: int):
     """Page table that lays each sequence's pages out back to back in order (no permutation)."""
     pages_per = [(int(c) + page_size - 1) // page_size for c in ctx_lens]

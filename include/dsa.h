@@ -123,6 +123,62 @@ dsa_status dsa_indexer_topk_paged(const uint8_t* q_idx, const float* w, const ui
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Batched prefill indexer + top-k over paged key caches: many sequences per call, each query
+ * row of any length of prefix (variable-length batches, and chunked prefill of a chunk of
+ * queries against the prefix already in the cache).  The serving layout is the 64-token paged
+ * cache of the mundobytes.com page (section "Quick guide to running locally"); the score and
+ * the selection are those of dsa_indexer_topk (jdon.com article, paragraphs on the lightning
+ * indexer and on fine-grained token selection).
+ *
+ * q_idx      [n_q, H_I, d_I]             FP8   indexer queries
+ * w          [n_q, H_I]                  fp32  head weights
+ * k_cache    [n_pages, page_size, d_I]   FP8   keys of all sequences (page_size a power of
+ *                                              two >= 8, else DSA_ERR_UNSUPPORTED_SHAPE),
+ *                                              written e.g. by dsa_cache_append
+ * page_table [n_seq, max_pages]          int32 logical row s of sequence b at page
+ *                                              page_table[b*max_pages + s/page_size]; an
+ *                                              entry outside [0, n_pages) in a row's range
+ *                                              reads as a page of zero keys
+ * q_seq      [n_q]                       int32 sequence of each query row (NULL: all 0); a
+ *                                              sequence outside [0, n_seq) selects nothing.
+ *                                              Rows sorted by sequence run fastest (a group of
+ *                                              16 consecutive rows streams the keys of each
+ *                                              sequence it touches in turn)
+ * q_pos      [n_q]                       int32 position t of each row in its sequence:
+ *                                              candidates s in [0, t], t clamped to
+ *                                              max_pages*page_size - 1; t < 0 selects nothing
+ * out_idx    [n_q, top_k]                int32 logical positions, ascending, then -1
+ * workspace: dsa_indexer_topk_workspace_size(n_q, top_k) bytes.  Precision and selection
+ * rules are those of dsa_indexer_topk.
+ * ------------------------------------------------------------------------------------- */
+dsa_status dsa_indexer_topk_batched(const uint8_t* q_idx, const float* w,
+                                    const uint8_t* k_cache, const int32_t* page_table,
+                                    int32_t n_seq, int32_t max_pages, int32_t n_pages,
+                                    int32_t page_size, const int32_t* q_seq,
+                                    const int32_t* q_pos, int32_t n_q, int32_t H_I, int32_t d_I,
+                                    int32_t top_k, int32_t* out_idx, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Batched sparse MQA over paged KV caches: row i (sequence q_seq[i], NULL: 0, position
+ * q_pos[i]) attends the selected rows of its sequence through the page table, as
+ * dsa_sparse_mqa_prefill does for one contiguous sequence (openi.cn page, MLA/MQA item;
+ * mundobytes.com page, "Quick guide to running locally" for the paging).
+ *
+ * q [n_q, H, D_k] bf16, kv_cache [n_pages, page_size, D_k] bf16, page_table [n_seq,
+ * max_pages], q_seq / q_pos [n_q], idx [n_q, top_k] logical positions (entries outside
+ * [0, t], or on a page-table entry outside [0, n_pages), are skipped), out [n_q, H, D_v]
+ * bf16, lse [n_q, H] fp32 or NULL.  A row of a sequence outside [0, n_seq) gets o = 0,
+ * lse = -inf.
+ * ------------------------------------------------------------------------------------- */
+dsa_status dsa_sparse_mqa_batched(const uint16_t* q, const uint16_t* kv_cache,
+                                  const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                                  int32_t n_pages, int32_t page_size, const int32_t* q_seq,
+                                  const int32_t* q_pos, const int32_t* idx, int32_t n_q,
+                                  int32_t H, int32_t D_k, int32_t D_v, int32_t top_k,
+                                  float scale, uint16_t* out, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Sparse MQA prefill over the selected rows of one contiguous sequence.
  *
  * q      [n_q, H, D_k]     bf16  queries

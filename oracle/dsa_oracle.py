@@ -269,6 +269,55 @@ def decode(inp: dict, seqs=None, idx=None):
     return out_idx, o, lse
 
 
+def batched_prefill(inp: dict, rows=None, idx=None):
+    """Prefill of many sequences whose keys and KV rows sit in paged caches: query row i is
+    position t = q_pos[i] of sequence b = q_seq[i] (all 0 when q_seq is absent) and reads that
+    sequence's rows 0..t through page_table[b].  Variable-length batches and chunked prefill
+    (queries of a chunk against the prefix already cached) are both this.  Returns
+    (idx [n,k], o [n,H,D_v], lse [n,H]) for the requested rows; ``idx`` may be given to run the
+    attention alone.  A row of a sequence outside the page table, or with t < 0, selects
+    nothing.  (Paging: mundobytes.com page, "Quick guide to running locally".)
+    """
+    pt = _np(inp["page_table"])
+    P = int(inp["page_size"])
+    q_pos = _np(inp["q_pos"]).astype(np.int64)
+    n = q_pos.shape[0]
+    q_seq = np.zeros(n, dtype=np.int64) if inp.get("q_seq") is None else \
+        _np(inp["q_seq"]).astype(np.int64)
+    rows = list(range(n)) if rows is None else list(rows)
+    k = int(inp["top_k"])
+    d_v = int(inp["D_v"]) if "D_v" in inp else 0
+    with_attn = "q" in inp and inp.get("q") is not None
+    kc = _np(inp["k_cache"])
+    kvc = _np(inp["kv_cache"]) if with_attn else None
+    q_codes = _np(inp["q_idx"])
+    w = _np(inp["w"]).astype(np.float64)
+    t_cap = pt.shape[1] * P - 1
+    out_idx = np.empty((len(rows), k), dtype=np.int32)
+    H = inp["q"].shape[1] if with_attn else 0
+    o = np.empty((len(rows), H, d_v))
+    lse = np.empty((len(rows), H))
+    for r, i in enumerate(rows):
+        b = int(q_seq[i])
+        t = min(int(q_pos[i]), t_cap)
+        if b < 0 or b >= pt.shape[0] or t < 0:
+            t = -1
+        if idx is not None:
+            out_idx[r] = np.asarray(idx[r])
+        elif t < 0:
+            out_idx[r] = -1
+        else:
+            keys = decode_e4m3fn(paged_rows(kc, pt[b], t + 1, P))
+            out_idx[r] = topk_select(indexer_scores(decode_e4m3fn(q_codes[i]), w[i], keys), k)
+        if with_attn:
+            sel = valid_selected(out_idx[r], t)
+            kv_sel = decode_bf16(paged_gather(kvc, pt[b], sel, P)) if len(sel) else \
+                np.zeros((0, kvc.shape[-1]))
+            o[r], lse[r] = sparse_mqa(decode_bf16(inp["q"][i]), kv_sel, d_v,
+                                      float(inp["scale"]))
+    return out_idx, o, lse
+
+
 # ----------------------------------------------------------------------------------------
 # Cache write: FP8 quantisation of new indexer keys and the paged append
 # ----------------------------------------------------------------------------------------
@@ -361,6 +410,6 @@ def selected_pairs(L: int, k: int) -> int:
 __all__ = [
     "E4M3FN", "decode_e4m3fn", "decode_bf16", "indexer_scores", "topk_select", "sparse_mqa",
     "valid_selected", "prefill_indexer_topk", "prefill", "paged_gather", "paged_rows", "decode",
-    "quantize_e4m3fn", "cache_append", "row_work",
+    "batched_prefill", "quantize_e4m3fn", "cache_append", "row_work",
     "causal_pairs", "selected_pairs",
 ]

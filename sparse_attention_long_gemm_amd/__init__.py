@@ -42,6 +42,10 @@ SIGNATURES = {
     "dsa_sparse_mqa_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "dsa_sparse_mqa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                              _F, _I, _P, _P, _P, _Z, _P]),
+    "dsa_indexer_topk_batched": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I,
+                                                _I, _I, _P, _P, _Z, _P]),
+    "dsa_sparse_mqa_batched": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I,
+                                              _I, _I, _F, _P, _P, _P]),
     "dsa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dsa_sparse_mqa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                      _I, _I, _I, _F, _I, _P, _P, _P]),
@@ -262,6 +266,67 @@ def sparse_mqa_decode(q, kv_cache, page_table, ctx_lens, idx, d_v: int, scale: f
     return out, lse
 
 
+def indexer_topk_batched(q_idx, w, k_cache, page_table, q_pos, top_k: int, q_seq=None,
+                         out=None, workspace=None):
+    """Batched prefill indexer + top-k over a paged FP8 key cache (dsa_indexer_topk_batched):
+    query row i of sequence q_seq[i] (default 0) at position q_pos[i]."""
+    lib = load_library()
+    _need(q_idx, "q_idx", _FP8, 3)
+    dev = q_idx.device
+    n_q, H_I, d_I = q_idx.shape
+    _need(w, "w", _F32, 2, dev, shape=(n_q, H_I))
+    _need(k_cache, "k_cache", _FP8, 3, dev)
+    _need(page_table, "page_table", _I32, 2, dev)
+    _need(q_pos, "q_pos", _I32, 1, dev, shape=(n_q,))
+    if q_seq is not None:
+        _need(q_seq, "q_seq", _I32, 1, dev, shape=(n_q,))
+    n_pages, page_size, dk = k_cache.shape
+    if dk != d_I:
+        raise ValueError("k_cache rows do not match q_idx")
+    if out is None:
+        out = torch.empty((n_q, top_k), dtype=torch.int32, device=dev)
+    _need(out, "out", _I32, 2, dev, shape=(n_q, top_k))
+    ws, nb = _workspace(indexer_topk_workspace_size(n_q, top_k), dev, workspace)
+    _check(lib.dsa_indexer_topk_batched(_ptr(q_idx), _ptr(w), _ptr(k_cache), _ptr(page_table),
+                                        page_table.shape[0], page_table.shape[1], n_pages,
+                                        page_size, _ptr(q_seq), _ptr(q_pos), n_q, H_I, d_I, top_k,
+                                        _ptr(out), _ptr(ws), nb, _stream(dev)),
+           "dsa_indexer_topk_batched")
+    return out
+
+
+def sparse_mqa_batched(q, kv_cache, page_table, q_pos, idx, d_v: int, scale: float, q_seq=None,
+                       out=None, lse=None, want_lse: bool = True):
+    """Batched sparse MQA over a paged bf16 KV cache (dsa_sparse_mqa_batched)."""
+    lib = load_library()
+    _need(q, "q", _BF16, 3)
+    dev = q.device
+    n_q, H, D_k = q.shape
+    _need(kv_cache, "kv_cache", _BF16, 3, dev)
+    _need(page_table, "page_table", _I32, 2, dev)
+    _need(q_pos, "q_pos", _I32, 1, dev, shape=(n_q,))
+    _need(idx, "idx", _I32, 2, dev)
+    if q_seq is not None:
+        _need(q_seq, "q_seq", _I32, 1, dev, shape=(n_q,))
+    n_pages, page_size, dk = kv_cache.shape
+    if dk != D_k or idx.shape[0] != n_q:
+        raise ValueError("inconsistent batched MQA shapes")
+    if out is None:
+        out = torch.empty((n_q, H, d_v), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, H), dtype=torch.float32, device=dev)
+    _need(out, "out", _BF16, 3, dev, shape=(n_q, H, d_v))
+    if lse is not None:
+        _need(lse, "lse", _F32, 2, dev, shape=(n_q, H))
+    _check(lib.dsa_sparse_mqa_batched(_ptr(q), _ptr(kv_cache), _ptr(page_table),
+                                      page_table.shape[0], page_table.shape[1], n_pages,
+                                      page_size, _ptr(q_seq), _ptr(q_pos), _ptr(idx), n_q, H, D_k,
+                                      d_v, idx.shape[1], float(scale), _ptr(out), _ptr(lse),
+                                      _stream(dev)),
+           "dsa_sparse_mqa_batched")
+    return out, lse
+
+
 def cache_append(page_table, pos, k_cache=None, kv_cache=None, k_new=None, kv_new=None,
                  seq=None):
     """Append new tokens to the paged caches (dsa_cache_append): k_new [T, d_I] bf16 is
@@ -343,6 +408,7 @@ def sparse_mqa_decode_noalloc(q, kv_cache, page_table, ctx_lens, idx, d_v: int, 
 
 __all__ = ["load_library", "DSAError", "indexer_topk", "indexer_topk_paged",
            "sparse_mqa_prefill", "sparse_mqa_decode", "sparse_mqa_decode_noalloc", "cache_append",
+           "indexer_topk_batched", "sparse_mqa_batched",
            "indexer_topk_workspace_size",
            "indexer_topk_paged_workspace_size", "sparse_mqa_decode_workspace_size",
            "SIGNATURES", "LIB_PATH"]

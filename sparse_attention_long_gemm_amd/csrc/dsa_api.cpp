@@ -124,6 +124,50 @@ dsa_status dsa_sparse_mqa_prefill(const uint16_t* q, const uint16_t* kv, int32_t
   return from_hip(dsa::launch_sparse_mqa(a, stream));
 }
 
+dsa_status dsa_indexer_topk_batched(const uint8_t* q_idx, const float* w,
+                                    const uint8_t* k_cache, const int32_t* page_table,
+                                    int32_t n_seq, int32_t max_pages, int32_t n_pages,
+                                    int32_t page_size, const int32_t* q_seq,
+                                    const int32_t* q_pos, int32_t n_q, int32_t H_I, int32_t d_I,
+                                    int32_t top_k, int32_t* out_idx, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (n_q < 0 || n_seq < 1 || !paging_ok(max_pages, n_pages, page_size))
+    return DSA_ERR_INVALID_ARG;
+  if (!indexer_shape_ok(H_I, d_I, top_k) || page_size < 8 || (page_size & (page_size - 1)) != 0)
+    return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (!q_idx || !w || !k_cache || !page_table || !q_pos || !out_idx || !workspace)
+    return DSA_ERR_INVALID_ARG;
+  if (workspace_bytes < dsa::indexer_prefill_ws(n_q, top_k)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(dsa::launch_indexer_topk_batched(q_idx, w, k_cache, page_table, n_seq,
+                                                   max_pages, n_pages, page_size, q_seq, q_pos,
+                                                   n_q, H_I, d_I, top_k, out_idx, workspace,
+                                                   stream));
+}
+
+dsa_status dsa_sparse_mqa_batched(const uint16_t* q, const uint16_t* kv_cache,
+                                  const int32_t* page_table, int32_t n_seq, int32_t max_pages,
+                                  int32_t n_pages, int32_t page_size, const int32_t* q_seq,
+                                  const int32_t* q_pos, const int32_t* idx, int32_t n_q,
+                                  int32_t H, int32_t D_k, int32_t D_v, int32_t top_k,
+                                  float scale, uint16_t* out, float* lse, hipStream_t stream) {
+  if (n_q < 0 || n_seq < 1 || !paging_ok(max_pages, n_pages, page_size) || !isfinite(scale))
+    return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > kMaxH || !dsa::mqa_shape_supported(D_k, D_v) || top_k < 1 ||
+      top_k > kMaxTopK)
+    return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (n_q > 0x7fffffff / 2 || !q || !kv_cache || !page_table || !q_pos || !idx || !out)
+    return DSA_ERR_INVALID_ARG;
+  dsa::MqaArgs a{};
+  a.q = q; a.kv = kv_cache; a.idx = idx; a.qpos_or_ctx = q_pos; a.page_table = page_table;
+  a.q_seq = q_seq; a.n_seq = n_seq; a.max_pages = max_pages; a.n_pages = n_pages;
+  a.page_size = page_size; a.n_kv = 0; a.n_q = n_q; a.H = H; a.D_k = D_k; a.D_v = D_v;
+  a.top_k = top_k; a.scale = scale; a.n_split = 1; a.rows_per_split = top_k; a.out = out;
+  a.lse = lse;
+  return from_hip(dsa::launch_sparse_mqa(a, stream));
+}
+
 dsa_status dsa_cache_append(const uint16_t* k_new, const uint16_t* kv_new, const int32_t* seq,
                             const int32_t* pos, const int32_t* page_table, int32_t T,
                             int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t d_I,

@@ -15,6 +15,12 @@ hipError_t launch_indexer_topk_prefill(const uint8_t* q_idx, const float* w, con
                                        int n_keys, const int32_t* q_pos, int n_q, int H_I,
                                        int d_I, int top_k, int32_t* out_idx, void* ws,
                                        hipStream_t stream);
+hipError_t launch_indexer_topk_batched(const uint8_t* q_idx, const float* w,
+                                       const uint8_t* k_cache, const int32_t* page_table,
+                                       int n_seq, int max_pages, int n_pages, int page_size,
+                                       const int32_t* q_seq, const int32_t* q_pos, int n_q,
+                                       int H_I, int d_I, int top_k, int32_t* out_idx, void* ws,
+                                       hipStream_t stream);
 hipError_t launch_indexer_topk_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_cache,
                                      const int32_t* page_table, const int32_t* ctx_lens, int B,
                                      int max_pages, int n_pages, int page_size, int H_I, int d_I,
@@ -33,6 +39,8 @@ struct MqaArgs {
   const int32_t* idx;
   const int32_t* qpos_or_ctx;  // prefill: q_pos; decode: ctx_lens
   const int32_t* page_table;   // nullptr: contiguous prefill
+  const int32_t* q_seq;        // batched prefill: row -> sequence (nullptr: all sequence 0)
+  int n_seq;                   // 0: decode (row qi = sequence qi); > 0: batched prefill rows
   int max_pages, n_pages, page_size;
   int n_kv;
   int n_q, H, D_k, D_v, top_k;

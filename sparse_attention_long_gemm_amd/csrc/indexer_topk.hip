@@ -92,6 +92,8 @@ struct PrefillShared {
   u32 hist[NWAVE][256];           // per-wave radix histograms
   u32 rhist[QB][256];             // per-row histogram of the listed scores (see RowHist)
   int full[2][NWAVE];             // [iteration parity][wave]: a row of the wave is near full
+  int seg_seq[QB];                // paged: each row's sequence until its segment ran, then -1
+  int seg_t[QB];                  // paged: each row's last candidate position
 };
 
 // Physical 16-byte chunk of logical chunk c (0..7) of key row r in a key tile: the XOR spreads
@@ -249,11 +251,21 @@ __device__ __forceinline__ void epi_abs(float* acc, const v4f& x, float wj) {
   acc[3] = fmaf(wj, __builtin_fabsf(x[3]), acc[3]);
 }
 
+// PAGED: the keys come from a paged cache [n_pages, page_size, d_I] through the page table
+// row of each query row's sequence (q_seq; NULL: every row is in sequence 0), page_size a
+// power of two >= 8 (2^page_shift) so that every 8-row wave-load lies in one page and the page
+// index is a shift; a page-table entry outside
+// [0, n_pages) reads as a page of zero keys.  A workgroup whose rows belong to several
+// sequences streams each sequence's keys in turn (rows of the other sequences masked).
+// Otherwise the keys are the contiguous rows k_idx [n_keys, d_I].
+template <bool PAGED>
 __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int n_q, int n_keys,
-    int H_I, int d_I, int top_k, int cap, float* __restrict__ cand_score,
-    int32_t* __restrict__ cand_pos, int32_t* __restrict__ out_idx) {
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ q_seq, int n_seq,
+    int max_pages, int n_pages, int page_shift, int H_I, int d_I, int top_k, int cap,
+    float* __restrict__ cand_score, int32_t* __restrict__ cand_pos,
+    int32_t* __restrict__ out_idx) {
   __shared__ PrefillShared sh;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -265,22 +277,33 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   const int q0 = blockIdx.x * QB;
   const bool heads_here = HPW * hg < H_I;
 
-  // ---- last candidate position of each row (t clamped to the keys; -1: nothing) ----
-  int t_lane = -1;
+  // ---- last candidate position t of each row (clamped to the keys; -1: nothing) and the
+  // sequence whose keys it reads (-1 for a row with nothing to score) ----
+  int t_lane = -1, seq_lane = -1;
   {
     const int q = q0 + c16;
-    if (q < n_q) t_lane = min(q_pos[q], n_keys - 1);
+    if (q < n_q) {
+      if (PAGED) {
+        const int sq = q_seq != nullptr ? q_seq[q] : 0;
+        if (sq >= 0 && sq < n_seq) {
+          seq_lane = sq;
+          t_lane = min(q_pos[q], (max_pages << page_shift) - 1);
+        }
+      } else {
+        seq_lane = 0;
+        t_lane = min(q_pos[q], n_keys - 1);
+      }
+    }
+    if (t_lane < 0) seq_lane = -1;
   }
-  int t_max = t_lane;
-  for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
-  // rows owned by this wave, their state (wave-uniform)
+  // rows owned by this wave, their state (wave-uniform); t_own is set per sequence segment
   int t_own[RPW], cnt[RPW];
   float thr[RPW];
   u32 hi_seen[RPW];   // per lane: largest order key this lane ever listed for the row
   RowHist rowh[RPW];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
-    t_own[rr] = __shfl(t_lane, RPW * wave + rr);
+    t_own[rr] = -1;
     cnt[rr] = 0;
     thr[rr] = -__builtin_inff();
     hi_seen[rr] = 0u;
@@ -342,24 +365,44 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   // whose rows have the same (row >> 1) & 7 pattern.  Keys past n_keys and chunks past d_I
   // are not loaded: the tiles are zeroed once, so chunks past d_I stay zero, and a key past
   // n_keys (whose slot may hold an older key) is past every row's last position t. ----
+  // Paged keys: wave-load j's 8 rows lie in one page; the wave looks the page up (a scalar
+  // load), and a page-table entry outside [0, n_pages) fills its LDS slots with zero keys
+  // instead.  Rows past the page table are not loaded (past every row's t).
   const int dl_row = lane >> 3;
   const int dl_chunk = (lane & 7) ^ ((4 * (wave & 1) + (dl_row >> 1)) & 7);
   const bool dl_chunk_ok = 16 * dl_chunk < d_I;
   const u32 dl_off = (u32)(dl_row * d_I + 16 * dl_chunk);
+  const int32_t* seg_pt = page_table;   // page-table row of the sequence being streamed
   auto dma_tile = [&](int it_, int b) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = __builtin_amdgcn_readfirstlane(wave) + NWAVE * jj;   // wave-uniform
       const int s0 = __builtin_amdgcn_readfirstlane(it_ * BK2 + 8 * j);
+      const uint8_t* src = k_idx + (size_t)s0 * d_I;
+      bool rows_ok = true;
+      if (PAGED) {
+        const int pi = s0 >> page_shift;        // page_size = 2^page_shift
+        int page = pi < max_pages ? seg_pt[pi] : -1;
+        page = __builtin_amdgcn_readfirstlane(page);
+        const bool page_ok = page >= 0 && page < n_pages;
+        if (!page_ok) {
+          if (pi < max_pages && dl_chunk_ok)   // inside the table: a page of zero keys
+            *reinterpret_cast<v4i*>(sh.ktile[b] + 1024 * j + 16 * lane) = v4i{0, 0, 0, 0};
+          continue;
+        }
+        src = k_idx + (((size_t)page << page_shift) + (s0 & ((1 << page_shift) - 1))) * d_I;
+      } else {
+        rows_ok = s0 + dl_row < n_keys;
+      }
       // 64-bit base in scalar registers: each half through readfirstlane (which returns a
       // signed int), widened as unsigned so the low half is not sign-extended
-      const uint64_t bp = (uint64_t)(uintptr_t)(k_idx + (size_t)s0 * d_I);
+      const uint64_t bp = (uint64_t)(uintptr_t)src;
       const uint64_t base =
           ((uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)(bp >> 32)) << 32) |
           (uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)bp);
       const u32 lds = __builtin_amdgcn_readfirstlane(
           (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(sh.ktile[b] + 1024 * j));
-      if (dl_chunk_ok && s0 + dl_row < n_keys) {
+      if (dl_chunk_ok && rows_ok) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
@@ -371,13 +414,9 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     }
   };
 
-  const int n_iter = (t_max + BK2) / BK2;  // key tiles covering keys 0..t_max
   for (int i = tid; i < 2 * BK2 * 128 / 16; i += NT)
     reinterpret_cast<v4i*>(&sh.ktile[0][0])[i] = v4i{0, 0, 0, 0};
-  __syncthreads();
-  dma_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  int n_iter = 0;   // key tiles of the current segment
 
   // Scores of key tile `kt` (keys [128 kt, 128 kt + 128)) from key buffer kt%2 into partial
   // buffer kt%2.
@@ -464,6 +503,14 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     if (lane == 0) sh.full[buf][wave] = full ? 1 : 0;
   };
 
+  // One segment: the rows whose t_own >= 0 stream the keys 0..t_max of one sequence.
+  auto run_segment = [&](int t_max) {
+  n_iter = (t_max + BK2) / BK2;   // key tiles covering keys 0..t_max
+  __syncthreads();                // the previous segment's last reads of both tiles are done
+  dma_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
   // Step `it` scores key tile it and filters key tile it-1 (scored in the previous step), then
   // synchronizes.  The two waves that share a SIMD (waves w and w+4, opposite tile parities)
   // take the two phases in opposite orders, so one wave's VALU-heavy filter runs beside the
@@ -511,6 +558,41 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next key tile has landed
     __syncthreads();
+  }
+  };
+
+  if constexpr (!PAGED) {
+    // contiguous keys: one segment, every row
+    int t_max = t_lane;
+    for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) t_own[rr] = __shfl(t_lane, RPW * wave + rr);
+    run_segment(t_max);
+  } else {
+    // Segments: the rows of one sequence at a time (one segment unless the workgroup's rows
+    // span sequences).  The rows' pending sequences wait in LDS, not in registers.
+    if (tid < QB) {
+      sh.seg_seq[tid] = seq_lane;   // lanes 0..15 of wave 0 hold rows 0..15 (c16 == tid)
+      sh.seg_t[tid] = t_lane;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (;;) {
+      const int pend = sh.seg_seq[c16];
+      const uint64_t left = wave_ballot(pend >= 0) & 0xffffull;   // lanes 0..15: the 16 rows
+      if (left == 0ull) break;
+      const int cur = __shfl(pend, __builtin_ctzll(left));
+      const bool act = pend == cur;
+      const int t_act = act ? sh.seg_t[c16] : -1;
+      int t_max = t_act;
+      for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) t_own[rr] = __shfl(t_act, RPW * wave + rr);
+      seg_pt = page_table + (size_t)cur * max_pages;
+      __syncthreads();              // every wave has read seg_seq before it changes
+      if (tid < QB && act) sh.seg_seq[tid] = -1;
+      run_segment(t_max);           // (its barriers publish the change)
+    }
   }
 
   // ---- final exact selection of this wave's rows ----
@@ -1272,8 +1354,27 @@ hipError_t launch_indexer_topk_prefill(const uint8_t* q_idx, const float* w, con
   float* cs = reinterpret_cast<float*>(ws);
   int32_t* ci = reinterpret_cast<int32_t*>(cs + (size_t)n_q * cap);
   const int grid = (n_q + QB - 1) / QB;
-  hipLaunchKernelGGL(indexer_topk_prefill_kernel, dim3(grid), dim3(NT), 0, stream, q_idx, w,
-                     k_idx, q_pos, n_q, n_keys, H_I, d_I, top_k, cap, cs, ci, out_idx);
+  hipLaunchKernelGGL(indexer_topk_prefill_kernel<false>, dim3(grid), dim3(NT), 0, stream, q_idx,
+                     w, k_idx, q_pos, n_q, n_keys, nullptr, nullptr, 1, 1, 1, 1, H_I, d_I,
+                     top_k, cap, cs, ci, out_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_topk_batched(const uint8_t* q_idx, const float* w,
+                                       const uint8_t* k_cache, const int32_t* page_table,
+                                       int n_seq, int max_pages, int n_pages, int page_size,
+                                       const int32_t* q_seq, const int32_t* q_pos, int n_q,
+                                       int H_I, int d_I, int top_k, int32_t* out_idx, void* ws,
+                                       hipStream_t stream) {
+  const int cap = indexer_cap(top_k);
+  float* cs = reinterpret_cast<float*>(ws);
+  int32_t* ci = reinterpret_cast<int32_t*>(cs + (size_t)n_q * cap);
+  const int grid = (n_q + QB - 1) / QB;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  hipLaunchKernelGGL(indexer_topk_prefill_kernel<true>, dim3(grid), dim3(NT), 0, stream, q_idx,
+                     w, k_cache, q_pos, n_q, 0, page_table, q_seq, n_seq, max_pages, n_pages,
+                     shift, H_I, d_I, top_k, cap, cs, ci, out_idx);
   return hipGetLastError();
 }
 

@@ -190,11 +190,16 @@ __host__ __device__ constexpr int vm_wait_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// PAGED rows read their KV rows through a page table: in decode (n_seq == 0) row qi is
+// sequence qi with t = ctx[qi] - 1; in a batched prefill (n_seq > 0) row qi is sequence
+// q_seq[qi] (0 when q_seq is NULL; a sequence outside [0, n_seq) attends nothing) with
+// t = q_pos[qi].
 template <int DK, int DV, bool PAGED>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ qpos_or_ctx,
-    const int32_t* __restrict__ page_table, int max_pages, int n_pages, int page_size, int n_kv,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ q_seq, int n_seq,
+    int max_pages, int n_pages, int page_size, int n_kv,
     int H, int top_k, float scale_log2, int n_split, int rows_per_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml) {
@@ -221,8 +226,14 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   const bool head_ok = head < H;
 
   int t;
+  int prow = qi;   // page-table row
   if (PAGED) {
-    t = qpos_or_ctx[qi] - 1;
+    if (n_seq > 0) {
+      prow = q_seq != nullptr ? q_seq[qi] : 0;
+      t = (prow >= 0 && prow < n_seq) ? qpos_or_ctx[qi] : -1;
+    } else {
+      t = qpos_or_ctx[qi] - 1;
+    }
     if (t > max_pages * page_size - 1) t = max_pages * page_size - 1;
   } else {
     t = qpos_or_ctx[qi];
@@ -261,7 +272,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const bool ok = sv[k] >= 0 && sv[k] <= t;
-      if (PAGED) pg[k] = ok ? page_table[(size_t)qi * max_pages + sv[k] / page_size] : -1;
+      if (PAGED) pg[k] = ok ? page_table[(size_t)prow * max_pages + sv[k] / page_size] : -1;
       else pg[k] = ok ? 0 : -1;
     }
 #pragma unroll
@@ -533,15 +544,15 @@ hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   if (a.page_table == nullptr) {
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false>), dim3(a.n_q, 1), dim3(NT), 0, stream,
-                       a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, 0, 0, 1, a.n_kv, a.H, a.top_k,
-                       scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr);
+                       a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0, 0, 1, a.n_kv,
+                       a.H, a.top_k, scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr);
     return hipGetLastError();
   }
   const int rps = a.rows_per_split;
   hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true>), dim3(a.n_q, a.n_split), dim3(NT), 0,
-                     stream, a.q, a.kv, a.idx, a.qpos_or_ctx, a.page_table, a.max_pages,
-                     a.n_pages, a.page_size, 0, a.H, a.top_k, scale_log2, a.n_split, rps, a.out,
-                     a.lse, a.part_o, a.part_ml);
+                     stream, a.q, a.kv, a.idx, a.qpos_or_ctx, a.page_table, a.q_seq, a.n_seq,
+                     a.max_pages, a.n_pages, a.page_size, 0, a.H, a.top_k, scale_log2,
+                     a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   // partial counts up to the ABI's limit of 16 splits

@@ -369,6 +369,53 @@ def test_cache_append_writes_the_slots_and_nothing_else():
         k_new.float().clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)))
 
 
+# --------------------------------------------------------------------------- batched prefill
+
+def _contiguous_of(d, b, rows):
+    """The contiguous single-sequence inputs of sequence b's query rows ``rows`` (data move)."""
+    L, off = d["seq_lens"][b], d["seq_off"][b]
+    return {"q_idx": d["q_idx"][rows], "w": d["w"][rows], "k_idx": d["k_flat"][off:off + L],
+            "q_pos": d["q_pos"][rows], "top_k": d["top_k"], "q": d["q"][rows],
+            "kv": d["kv_flat"][off:off + L], "D_v": d["D_v"], "scale": d["scale"]}
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_batched_prefill_equals_each_sequence_prefilled_alone(seed):
+    """Variable-length sequences (one prefilled from 0, one as a chunk against a cached
+    prefix, one short) in random pages, with the query rows in a shuffled order: every row
+    equals the contiguous single-sequence prefill of its own sequence."""
+    sp = gi.BatchedSpec(seq_lens=(300, 700, 129), q_start=(0, 500, 0),
+                        idx=gi.IndexerSpec(H_I=4, d_I=32, grid_lo=-3, grid_hi=3, grid_step=0.125,
+                                           w_choices=(0.25, 0.5, 1.0), top_k=64),
+                        mqa=gi.MqaSpec(H=4, D_k=96, D_v=64, sigma=1.0, scale=96 ** -0.5),
+                        seed=seed)
+    n = 300 + 200 + 129
+    order = torch.randperm(n, generator=torch.Generator().manual_seed(seed))
+    d = gi.batched_inputs(sp, row_order=order)
+    i1, o1, l1 = orc.batched_prefill(d)
+    q_seq = d["q_seq"].numpy()
+    for b in range(3):
+        rows = np.flatnonzero(q_seq == b)
+        i2, o2, l2 = orc.prefill(_contiguous_of(d, b, torch.as_tensor(rows)))
+        assert np.array_equal(i1[rows], i2)
+        assert np.allclose(o1[rows], o2, rtol=0, atol=1e-13)
+        assert np.allclose(l1[rows], l2, rtol=0, atol=1e-13)
+
+
+def test_batched_prefill_rows_without_a_sequence_select_nothing():
+    sp = gi.BatchedSpec(seq_lens=(200,), idx=gi.IndexerSpec(H_I=4, d_I=32, top_k=16),
+                        mqa=gi.MqaSpec(H=2, D_k=64, D_v=64, sigma=1.0, scale=0.125))
+    d = gi.batched_inputs(sp)
+    d["q_seq"] = d["q_seq"].clone()
+    d["q_seq"][5] = 3
+    d["q_seq"][6] = -1
+    d["q_pos"] = d["q_pos"].clone()
+    d["q_pos"][7] = -4
+    idx, o, lse = orc.batched_prefill(d, rows=[5, 6, 7, 8])
+    assert (idx[:3] == -1).all() and (o[:3] == 0).all() and np.isneginf(lse[:3]).all()
+    assert (idx[3, :9] == np.arange(9)).all()
+
+
 # --------------------------------------------------------------------------- generators
 
 def test_generators_are_seeded_and_on_grid():
