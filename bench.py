@@ -124,6 +124,27 @@ class Decode:
         self.flops_idx = sum(2.0 * 64 * 128 * c for c in ctx)
         self.flops_mqa = sum(2.0 * m.H * (m.D_k + m.D_v) * min(kk, c) for c in ctx)
 
+    def setup_append(self):
+        """The new token of each sequence (position ctx-1) as it leaves its projections: the
+        indexer key in bf16 (values on the FP8 grid, so the cached key is unchanged) and the
+        latent KV row (the cached one), written back by dsa_cache_append."""
+        d = self.inp
+        P = d["page_size"]
+        pos = (d["ctx"] - 1).long()
+        pages = d["page_table"][torch.arange(self.sp.B, device=pos.device), pos // P].long()
+        self.app_pos = pos.to(torch.int32)
+        self.app_k = d["k_cache"][pages, pos % P].view(torch.float8_e4m3fn).to(torch.bfloat16)
+        self.app_kv = d["kv_cache"][pages, pos % P].contiguous()
+        m, ix = self.sp.mqa, self.sp.idx
+        # bytes per token: bf16 key + KV row read, FP8 key + KV row written, position and the
+        # page-table entry read
+        self.bytes_append = self.sp.B * (2 * ix.d_I + 2 * m.D_k + ix.d_I + 2 * m.D_k + 8)
+
+    def run_append(self):
+        d = self.inp
+        self.dsa.cache_append(d["page_table"], self.app_pos, k_cache=d["k_cache"],
+                              kv_cache=d["kv_cache"], k_new=self.app_k, kv_new=self.app_kv)
+
     def run(self, events=None):
         d, dsa = self.inp, self.dsa
         if events is not None:
@@ -135,6 +156,85 @@ class Decode:
         dsa.sparse_mqa_decode(d["q"], d["kv_cache"], d["page_table"], d["ctx"], self.idx,
                               d["D_v"], d["scale"], out=self.out, lse=self.lse,
                               workspace=self.ws_mqa)
+        if events is not None:
+            events[2].record()
+
+
+class ChunkedPaged:
+    """The same L=131072 prefill, chunk by chunk (4096 queries per call) against the growing
+    prefix held in 64-token pages (random page order): dsa_indexer_topk_batched +
+    dsa_sparse_mqa_batched.  Same rows, same work as ``Prefill``; the difference is the paging."""
+
+    def __init__(self, pre: Prefill, dev, seed=0, page_size=64):
+        self.pre, self.dsa = pre, pre.dsa
+        d = pre.inp
+        L, P = pre.L, page_size
+        n_pages = (L + P - 1) // P
+        g = torch.Generator().manual_seed(seed + 77)
+        perm = torch.randperm(n_pages, generator=g).to(torch.int32)
+        self.pt = perm[None, :].to(dev)
+        self.k_cache = torch.zeros((n_pages, P, d["k_idx"].shape[1]), dtype=torch.uint8,
+                                   device=dev)
+        self.kv_cache = torch.zeros((n_pages, P, d["kv"].shape[1]), dtype=torch.bfloat16,
+                                    device=dev)
+        gi.contiguous_to_pages(d["k_idx"], self.pt.cpu(), 0, n_pages, P, self.k_cache)
+        gi.contiguous_to_pages(d["kv"], self.pt.cpu(), 0, n_pages, P, self.kv_cache)
+        self.out = torch.empty_like(pre.out)
+        self.lse = torch.empty_like(pre.lse)
+
+    def run(self, events=None):
+        d, dsa, pre = self.pre.inp, self.dsa, self.pre
+        if events is not None:
+            events[0].record()
+        for a, e in pre.blocks:
+            dsa.indexer_topk_batched(d["q_idx"][a:e], d["w"][a:e], self.k_cache, self.pt,
+                                     d["q_pos"][a:e], pre.top_k, out=pre.idx[: e - a],
+                                     workspace=pre.ws)
+            dsa.sparse_mqa_batched(d["q"][a:e], self.kv_cache, self.pt, d["q_pos"][a:e],
+                                   pre.idx[: e - a], pre.wl.mqa.D_v, pre.wl.mqa.scale,
+                                   out=self.out[a:e], lse=self.lse[a:e])
+        if events is not None:
+            events[1].record()
+
+
+class Varlen:
+    """A variable-length batch prefilled in one call pair: 32 sequences, lengths uniform in
+    [1024, 8192] (seeded), keys and KV rows in 64-token pages."""
+
+    def __init__(self, dev, seed=0, n_seq=32):
+        import sparse_attention_long_gemm_amd as dsa
+        self.dsa = dsa
+        g = torch.Generator().manual_seed(seed + 5)
+        lens = torch.randint(1024, 8193, (n_seq,), generator=g).tolist()
+        self.sp = gi.BatchedSpec(seq_lens=tuple(lens), seed=seed)
+        self.inp = gi.batched_inputs(self.sp, device=dev)
+        d = self.inp
+        n_q = d["q_pos"].shape[0]
+        k = d["top_k"]
+        self.idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((n_q, self.sp.mqa.H, self.sp.mqa.D_v), dtype=torch.bfloat16,
+                               device=dev)
+        self.lse = torch.empty((n_q, self.sp.mqa.H), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(dsa.indexer_topk_workspace_size(n_q, k), dtype=torch.uint8,
+                              device=dev)
+        self.tokens = n_q
+        ix, m = self.sp.idx, self.sp.mqa
+        self.flops_idx = sum(2.0 * ix.H_I * ix.d_I * causal_pairs_range(0, n) for n in lens)
+        self.flops_mqa = sum(2.0 * m.H * (m.D_k + m.D_v) * selected_pairs_range(0, n, k)
+                             for n in lens)
+        self.lens = lens
+
+    def run(self, events=None):
+        d, dsa = self.inp, self.dsa
+        if events is not None:
+            events[0].record()
+        dsa.indexer_topk_batched(d["q_idx"], d["w"], d["k_cache"], d["page_table"], d["q_pos"],
+                                 d["top_k"], q_seq=d["q_seq"], out=self.idx, workspace=self.ws)
+        if events is not None:
+            events[1].record()
+        dsa.sparse_mqa_batched(d["q"], d["kv_cache"], d["page_table"], d["q_pos"], self.idx,
+                               self.sp.mqa.D_v, self.sp.mqa.scale, q_seq=d["q_seq"],
+                               out=self.out, lse=self.lse)
         if events is not None:
             events[2].record()
 
@@ -263,6 +363,174 @@ def cpu_baseline(prefill: Prefill, budget_s: float = 20.0):
                       f"min(k,t+1)*2*H*(D_k+D_v)"}
 
 
+def extra_legs(pre: Prefill, dec: Decode, dev, reps: int):
+    """The next rows of the path, each timed on its own (not part of the step above):
+    the 128K prefill chunk by chunk through paged caches, a variable-length batch, and the
+    decode step's cache append."""
+    out = {}
+    ch = ChunkedPaged(pre, dev)
+    ch.run()
+    t = _time(ch.run, reps) * 1e-3
+    F_idx, F_mqa = sum(pre.flops_idx), sum(pre.flops_mqa)
+    roof = F_idx / PEAK_FP8 + F_mqa / PEAK_BF16
+    out["chunked_paged_prefill"] = {
+        "workload": "L=131072 in 32 chunks of 4096 against 64-token pages (random order)",
+        "ms": t * 1e3, "tokens_per_s": pre.L / t, "frac_of_roofline": roof / t}
+    del ch
+    torch.cuda.empty_cache()
+    vl = Varlen(dev)
+    vl.run()
+    ev = [[_ev(), _ev(), _ev()] for _ in range(reps)]
+    for e in ev:
+        vl.run(e)
+    torch.cuda.synchronize()
+    t_i = sum(e[0].elapsed_time(e[1]) for e in ev) / reps * 1e-3
+    t_m = sum(e[1].elapsed_time(e[2]) for e in ev) / reps * 1e-3
+    out["varlen_prefill"] = {
+        "workload": f"{len(vl.lens)} sequences, lengths U[1024, 8192] (sum {sum(vl.lens)}), "
+                    "one batched call pair over 64-token pages",
+        "ms": (t_i + t_m) * 1e3, "tokens_per_s": vl.tokens / (t_i + t_m),
+        "indexer_frac": vl.flops_idx / t_i / PEAK_FP8, "mqa_frac": vl.flops_mqa / t_m / PEAK_BF16,
+        "frac_of_roofline": (vl.flops_idx / PEAK_FP8 + vl.flops_mqa / PEAK_BF16) / (t_i + t_m)}
+    del vl
+    torch.cuda.empty_cache()
+    dec.setup_append()
+    dec.run_append()
+    t = _time(dec.run_append, max(reps, 5)) * 1e-3
+    out["cache_append"] = {"workload": f"decode step's new tokens, B={dec.sp.B}",
+                           "us": t * 1e6, "bytes": dec.bytes_append,
+                           "achieved_gbps": dec.bytes_append / t / 1e9}
+    return out
+
+
+_BUSY = {}
+
+
+def _time(fn, reps):
+    """Mean milliseconds of fn() over reps launches, HIP events on the current stream.  A
+    millisecond of unrelated GPU work is queued first, so that the host has enqueued the timed
+    launches before the GPU reaches them (the events then see GPU time, not launch latency)."""
+    dev = torch.cuda.current_device()
+    if dev not in _BUSY:
+        _BUSY[dev] = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    _BUSY[dev].add_(1.0)
+    evs = [(_ev(), _ev()) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+USD_PER_GPU_HOUR = 2.0   # the pricing unit of the pages' cost-per-token figures
+
+
+def curves(dev, reps: int = 3, block: int = 256):
+    """Cost per token against token position, DSA next to dense causal attention, on the same
+    shapes (H=128, D_k=576, D_v=512; H_I=64, d_I=128, k=2048):
+      prefill: a block of `block` query rows ending at position p (keys [0, p)): DSA = indexer +
+               top-k + sparse MQA, dense = dense MQA over all earlier positions;
+      decode:  a step of B=64 sequences all at context length p: DSA = paged indexer + top-k +
+               sparse MQA, dense = dense MQA over the whole context.
+    Reported as microseconds per token and as dollars per million tokens at $2 per GPU-hour."""
+    import sparse_attention_long_gemm_amd as dsa
+    dsa.load_library()
+    L = 131072
+    points = [4096, 8192, 16384, 32768, 65536, 98304, 131072]
+    pre = Prefill(L=L, block=block, dev=dev)
+    d, wl = pre.inp, pre.wl
+    m = wl.mqa
+    H, D_v, k = m.H, m.D_v, pre.top_k
+    o = torch.empty((block, H, D_v), dtype=torch.bfloat16, device=dev)
+    ls = torch.empty((block, H), dtype=torch.float32, device=dev)
+    ws_dense = torch.empty(max(1, dsa.dense_mqa_workspace_size(block, H, D_v, L)),
+                           dtype=torch.uint8, device=dev)
+    rows = []
+    for p in points:
+        a, e = p - block, p
+        def dsa_block():
+            dsa.indexer_topk(d["q_idx"][a:e], d["w"][a:e], d["k_idx"][:e], d["q_pos"][a:e], k,
+                             out=pre.idx[:block], workspace=pre.ws)
+            dsa.sparse_mqa_prefill(d["q"][a:e], d["kv"][:e], pre.idx[:block], d["q_pos"][a:e],
+                                   D_v, m.scale, out=o, lse=ls)
+
+        def dense_block():
+            dsa.dense_mqa_prefill(d["q"][a:e], d["kv"][:e], d["q_pos"][a:e], D_v, m.scale,
+                                  out=o, lse=ls, workspace=ws_dense)
+        dsa_block(), dense_block()
+        t_dsa, t_dense = _time(dsa_block, reps), _time(dense_block, reps)
+        f_dense = 2.0 * H * (576 + D_v) * causal_pairs_range(a, e)
+        rows.append({"phase": "prefill", "position": p, "dsa_us_per_token": t_dsa * 1e3 / block,
+                     "dense_us_per_token": t_dense * 1e3 / block,
+                     "dense_mfma_frac": f_dense / (t_dense * 1e-3) / PEAK_BF16})
+        print(f"[curves] prefill p={p}: dsa {t_dsa:.3f} ms dense {t_dense:.3f} ms",
+              file=sys.stderr, flush=True)
+    del pre, ws_dense
+    torch.cuda.empty_cache()
+    B = 64
+    sp = gi.DecodeSpec(B=B, ctx_lo=L, ctx_hi=L)
+    dd = gi.decode_inputs(sp, device=dev, ctx_lens=[L] * B)
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    od = torch.empty((B, H, D_v), dtype=torch.bfloat16, device=dev)
+    ld = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws_i = torch.empty(dsa.indexer_topk_paged_workspace_size(B, dd["max_pages"], 64),
+                       dtype=torch.uint8, device=dev)
+    ws_m = torch.empty(max(1, dsa.sparse_mqa_decode_workspace_size(B, H, D_v, k)),
+                       dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, dsa.dense_mqa_workspace_size(B, H, D_v, dd["max_pages"] * 64)),
+                       dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB: evicts the MALL
+    for p in points:
+        ctx = torch.full((B,), p, dtype=torch.int32, device=dev)
+        # the page table as wide as this context (the dense split count and the indexer's
+        # score rows follow the table's width; the host does not read the context lengths)
+        pt = dd["page_table"][:, : (p + 63) // 64].contiguous()
+
+        def dsa_step():
+            flush.add_(1.0)
+            dsa.indexer_topk_paged(dd["q_idx"], dd["w"], dd["k_cache"], pt, ctx, k,
+                                   out=idx, workspace=ws_i)
+            dsa.sparse_mqa_decode(dd["q"], dd["kv_cache"], pt, ctx, idx, D_v,
+                                  m.scale, out=od, lse=ld, workspace=ws_m)
+
+        def dense_step():
+            flush.add_(1.0)
+            dsa.dense_mqa_decode(dd["q"], dd["kv_cache"], pt, ctx, D_v, m.scale,
+                                 out=od, lse=ld, workspace=ws_d)
+
+        def flush_only():
+            flush.add_(1.0)
+        dsa_step(), dense_step()
+        t_f = _time(flush_only, reps)
+        t_dsa = _time(dsa_step, reps) - t_f
+        t_dense = _time(dense_step, reps) - t_f
+        rows.append({"phase": "decode", "position": p, "batch": B,
+                     "dsa_us_per_token": t_dsa * 1e3 / B, "dense_us_per_token": t_dense * 1e3 / B,
+                     "dense_hbm_frac": B * p * 1152 / (t_dense * 1e-3) / PEAK_HBM})
+        print(f"[curves] decode ctx={p}: dsa {t_dsa:.3f} ms dense {t_dense:.3f} ms",
+              file=sys.stderr, flush=True)
+    for r in rows:
+        r["dsa_usd_per_mtok"] = r["dsa_us_per_token"] * USD_PER_GPU_HOUR / 3600.0
+        r["dense_usd_per_mtok"] = r["dense_us_per_token"] * USD_PER_GPU_HOUR / 3600.0
+        r["dense_over_dsa"] = r["dense_us_per_token"] / r["dsa_us_per_token"]
+    return {"curves": rows, "prefill_block": block, "decode_batch": B,
+            "usd_per_gpu_hour": USD_PER_GPU_HOUR, "reps": reps}
+
+
+def curves_markdown(res) -> str:
+    lines = ["| phase | position | DSA µs/token | dense µs/token | dense / DSA | DSA $/Mtok | "
+             "dense $/Mtok | dense kernel roofline frac |", "|---|---|---|---|---|---|---|---|"]
+    for r in res["curves"]:
+        fr = r.get("dense_mfma_frac", r.get("dense_hbm_frac"))
+        kind = "MFMA" if "dense_mfma_frac" in r else "HBM"
+        lines.append(f"| {r['phase']} | {r['position']} | {r['dsa_us_per_token']:.3f} | "
+                     f"{r['dense_us_per_token']:.3f} | {r['dense_over_dsa']:.2f} | "
+                     f"{r['dsa_usd_per_mtok']:.5f} | {r['dense_usd_per_mtok']:.5f} | "
+                     f"{fr:.2f} ({kind}) |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +540,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy kernel used to scale the HBM byte counters")
+    ap.add_argument("--curves", action="store_true",
+                    help="only measure cost per token against position, DSA and dense")
+    ap.add_argument("--curves-md", default=None, help="also write the curves as a markdown table")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the chunked, variable-length and cache-append legs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the DSA path here is a single-GPU build "
@@ -282,6 +555,13 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(dev)
+        return
+    if args.curves:
+        res = curves(dev)
+        if args.curves_md:
+            with open(args.curves_md, "w") as fh:
+                fh.write(curves_markdown(res))
+        print(json.dumps(res), flush=True)
         return
     import sparse_attention_long_gemm_amd as dsa
     dsa.load_library()
@@ -367,6 +647,8 @@ def main():
         "decode": decode,
         "roofline": dominant,
     }
+    if not args.no_extra:
+        res["extra"] = extra_legs(pre, dec, dev, max(1, args.steps))
     ceil = measured_ceilings(dsa, dev)
     res["ceilings"] = ceil
     roof_idx["frac_of_measured"] = roof_idx["achieved"] / ceil["fp8_mfma_tflops"]

@@ -218,6 +218,38 @@ dsa_status dsa_sparse_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
                                  size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Dense causal MLA/MQA attention: the baseline the selection is measured against.  Every
+ * query row attends all positions 0..t (what DSA replaces by the top_k selected ones: the
+ * O(L^2) -> O(L k) step of the jdon.com "DeepSeek-V3.2-Exp" article, and its paragraph on
+ * inference cost comparing the two per token position).  Same shapes, layouts and numerics
+ * as the sparse calls (bf16 MFMA, fp32 softmax and accumulation); the positions of a row are
+ * split over workgroups of 2048 and merged by their log-sum-exp through the workspace.
+ *
+ * dsa_dense_mqa_prefill: q [n_q, H, D_k], kv [n_kv, D_k], q_pos [n_q] (t clamped to n_kv-1,
+ *   t < 0 attends nothing), out [n_q, H, D_v], lse [n_q, H] or NULL;
+ *   workspace >= dsa_dense_mqa_workspace_size(n_q, H, D_v, n_kv) bytes.
+ * dsa_dense_mqa_decode: one query per sequence over its positions [0, ctx) through the page
+ *   table (as dsa_sparse_mqa_decode; positions on a page-table entry outside [0, n_pages)
+ *   are skipped); workspace >= dsa_dense_mqa_workspace_size(B, H, D_v,
+ *   max_pages * page_size) bytes.
+ * The workspace size is 0 when max_len <= 2048 (no split); more than 65535 splits
+ * (max_len > 2^27) returns DSA_ERR_UNSUPPORTED_SHAPE.
+ * ------------------------------------------------------------------------------------- */
+size_t dsa_dense_mqa_workspace_size(int32_t n_q, int32_t H, int32_t D_v, int32_t max_len);
+
+dsa_status dsa_dense_mqa_prefill(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
+                                 const int32_t* q_pos, int32_t n_q, int32_t H, int32_t D_k,
+                                 int32_t D_v, float scale, uint16_t* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+dsa_status dsa_dense_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
+                                const int32_t* page_table, const int32_t* ctx_lens, int32_t B,
+                                int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t H,
+                                int32_t D_k, int32_t D_v, float scale, uint16_t* out,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Cache write: append new tokens to the paged caches the decode calls read.  Defines the step
  * just before the paged indexer and attention: the indexer keeps its keys in FP8 (jdon.com
  * "DeepSeek-V3.2-Exp" article, paragraph on the lightning indexer) in 64-token pages

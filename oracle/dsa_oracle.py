@@ -269,6 +269,46 @@ def decode(inp: dict, seqs=None, idx=None):
     return out_idx, o, lse
 
 
+def dense_prefill(inp: dict, rows=None):
+    """Dense causal attention, the baseline DSA replaces: row t attends every position 0..t
+    (t = q_pos, clamped to the KV rows; t < 0 attends nothing).  Returns (o [n,H,D_v],
+    lse [n,H]).  (jdon.com article: core attention goes from O(L^2) to O(L k); its
+    inference-cost paragraph compares the two per token position.)
+    """
+    q_pos = _np(inp["q_pos"]).astype(np.int64)
+    rows = list(range(q_pos.shape[0])) if rows is None else list(rows)
+    kv = _np(inp["kv"])
+    d_v, scale = int(inp["D_v"]), float(inp["scale"])
+    H = inp["q"].shape[1]
+    o = np.empty((len(rows), H, d_v))
+    lse = np.empty((len(rows), H))
+    for r, i in enumerate(rows):
+        t = min(int(q_pos[i]), kv.shape[0] - 1)
+        kv_all = decode_bf16(kv[: t + 1]) if t >= 0 else np.zeros((0, kv.shape[1]))
+        o[r], lse[r] = sparse_mqa(decode_bf16(inp["q"][i]), kv_all, d_v, scale)
+    return o, lse
+
+
+def dense_decode(inp: dict, seqs=None):
+    """Dense attention of each sequence's new query (t = ctx - 1) over its positions [0, ctx),
+    read through the page table.  Returns (o [B,H,D_v], lse [B,H])."""
+    ctx = _np(inp["ctx"]).astype(np.int64)
+    pt = _np(inp["page_table"])
+    P = int(inp["page_size"])
+    seqs = list(range(ctx.shape[0])) if seqs is None else list(seqs)
+    kvc = _np(inp["kv_cache"])
+    d_v, scale = int(inp["D_v"]), float(inp["scale"])
+    H = inp["q"].shape[1]
+    o = np.empty((len(seqs), H, d_v))
+    lse = np.empty((len(seqs), H))
+    for r, b in enumerate(seqs):
+        n = int(ctx[b])
+        kv_all = decode_bf16(paged_rows(kvc, pt[b], n, P)) if n > 0 else \
+            np.zeros((0, kvc.shape[-1]))
+        o[r], lse[r] = sparse_mqa(decode_bf16(inp["q"][b]), kv_all, d_v, scale)
+    return o, lse
+
+
 def batched_prefill(inp: dict, rows=None, idx=None):
     """Prefill of many sequences whose keys and KV rows sit in paged caches: query row i is
     position t = q_pos[i] of sequence b = q_seq[i] (all 0 when q_seq is absent) and reads that
@@ -410,6 +450,7 @@ def selected_pairs(L: int, k: int) -> int:
 __all__ = [
     "E4M3FN", "decode_e4m3fn", "decode_bf16", "indexer_scores", "topk_select", "sparse_mqa",
     "valid_selected", "prefill_indexer_topk", "prefill", "paged_gather", "paged_rows", "decode",
-    "batched_prefill", "quantize_e4m3fn", "cache_append", "row_work",
+    "batched_prefill", "dense_prefill", "dense_decode", "quantize_e4m3fn", "cache_append",
+    "row_work",
     "causal_pairs", "selected_pairs",
 ]

@@ -46,6 +46,11 @@ SIGNATURES = {
                                                 _I, _I, _P, _P, _Z, _P]),
     "dsa_sparse_mqa_batched": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I,
                                               _I, _I, _F, _P, _P, _P]),
+    "dsa_dense_mqa_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "dsa_dense_mqa_prefill": (ctypes.c_int, [_P, _P, _I, _P, _I, _I, _I, _I, _F, _P, _P, _P, _Z,
+                                             _P]),
+    "dsa_dense_mqa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P,
+                                            _P, _P, _Z, _P]),
     "dsa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dsa_sparse_mqa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                      _I, _I, _I, _F, _I, _P, _P, _P]),
@@ -327,6 +332,66 @@ def sparse_mqa_batched(q, kv_cache, page_table, q_pos, idx, d_v: int, scale: flo
     return out, lse
 
 
+def dense_mqa_workspace_size(n_q: int, H: int, d_v: int, max_len: int) -> int:
+    return int(load_library().dsa_dense_mqa_workspace_size(n_q, H, d_v, max_len))
+
+
+def dense_mqa_prefill(q, kv, q_pos, d_v: int, scale: float, out=None, lse=None,
+                      want_lse: bool = True, workspace=None):
+    """Dense causal attention of every query row over positions 0..t (the baseline)."""
+    lib = load_library()
+    _need(q, "q", _BF16, 3)
+    dev = q.device
+    n_q, H, D_k = q.shape
+    _need(kv, "kv", _BF16, 2, dev)
+    _need(q_pos, "q_pos", _I32, 1, dev, shape=(n_q,))
+    if kv.shape[1] != D_k:
+        raise ValueError("kv rows do not match q")
+    if out is None:
+        out = torch.empty((n_q, H, d_v), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, H), dtype=torch.float32, device=dev)
+    _need(out, "out", _BF16, 3, dev, shape=(n_q, H, d_v))
+    if lse is not None:
+        _need(lse, "lse", _F32, 2, dev, shape=(n_q, H))
+    ws, nb = _workspace(dense_mqa_workspace_size(n_q, H, d_v, kv.shape[0]), dev, workspace)
+    _check(lib.dsa_dense_mqa_prefill(_ptr(q), _ptr(kv), kv.shape[0], _ptr(q_pos), n_q, H, D_k,
+                                     d_v, float(scale), _ptr(out), _ptr(lse), _ptr(ws), nb,
+                                     _stream(dev)),
+           "dsa_dense_mqa_prefill")
+    return out, lse
+
+
+def dense_mqa_decode(q, kv_cache, page_table, ctx_lens, d_v: int, scale: float, out=None,
+                     lse=None, want_lse: bool = True, workspace=None):
+    """Dense attention of one query per sequence over its positions [0, ctx) (the baseline)."""
+    lib = load_library()
+    _need(q, "q", _BF16, 3)
+    dev = q.device
+    B, H, D_k = q.shape
+    _need(kv_cache, "kv_cache", _BF16, 3, dev)
+    _need(page_table, "page_table", _I32, 2, dev)
+    _need(ctx_lens, "ctx_lens", _I32, 1, dev, shape=(B,))
+    n_pages, page_size, dk = kv_cache.shape
+    if dk != D_k or page_table.shape[0] != B:
+        raise ValueError("inconsistent dense decode shapes")
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _need(out, "out", _BF16, 3, dev, shape=(B, H, d_v))
+    if lse is not None:
+        _need(lse, "lse", _F32, 2, dev, shape=(B, H))
+    max_len = page_table.shape[1] * page_size
+    ws, nb = _workspace(dense_mqa_workspace_size(B, H, d_v, max_len), dev, workspace)
+    _check(lib.dsa_dense_mqa_decode(_ptr(q), _ptr(kv_cache), _ptr(page_table), _ptr(ctx_lens), B,
+                                    page_table.shape[1], n_pages, page_size, H, D_k, d_v,
+                                    float(scale), _ptr(out), _ptr(lse), _ptr(ws), nb,
+                                    _stream(dev)),
+           "dsa_dense_mqa_decode")
+    return out, lse
+
+
 def cache_append(page_table, pos, k_cache=None, kv_cache=None, k_new=None, kv_new=None,
                  seq=None):
     """Append new tokens to the paged caches (dsa_cache_append): k_new [T, d_I] bf16 is
@@ -408,7 +473,8 @@ def sparse_mqa_decode_noalloc(q, kv_cache, page_table, ctx_lens, idx, d_v: int, 
 
 __all__ = ["load_library", "DSAError", "indexer_topk", "indexer_topk_paged",
            "sparse_mqa_prefill", "sparse_mqa_decode", "sparse_mqa_decode_noalloc", "cache_append",
-           "indexer_topk_batched", "sparse_mqa_batched",
+           "indexer_topk_batched", "sparse_mqa_batched", "dense_mqa_prefill",
+           "dense_mqa_decode", "dense_mqa_workspace_size",
            "indexer_topk_workspace_size",
            "indexer_topk_paged_workspace_size", "sparse_mqa_decode_workspace_size",
            "SIGNATURES", "LIB_PATH"]

@@ -168,6 +168,68 @@ dsa_status dsa_sparse_mqa_batched(const uint16_t* q, const uint16_t* kv_cache,
   return from_hip(dsa::launch_sparse_mqa(a, stream));
 }
 
+size_t dsa_dense_mqa_workspace_size(int32_t n_q, int32_t H, int32_t D_v, int32_t max_len) {
+  if (n_q < 0 || H < 1 || D_v < 1 || max_len < 0) return 0;
+  const int rps = dsa::dense_rows_per_split();
+  const long long ns = ((long long)max_len + rps - 1) / rps;
+  if (ns <= 1) return 0;
+  return (size_t)n_q * (size_t)ns * H * ((size_t)D_v * sizeof(uint16_t) + 2 * sizeof(float));
+}
+
+namespace {
+
+// Shared by the two dense entry points: split count, checks and launch.
+dsa_status dense_launch(dsa::MqaArgs& a, int32_t max_len, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  const int rps = dsa::dense_rows_per_split();
+  const long long ns = ((long long)max_len + rps - 1) / rps;
+  if (ns > 65535) return DSA_ERR_UNSUPPORTED_SHAPE;
+  a.n_split = ns < 1 ? 1 : (int)ns;
+  a.rows_per_split = rps;
+  const size_t need = dsa_dense_mqa_workspace_size(a.n_q, a.H, a.D_v, max_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if (a.n_split > 1) {
+    a.part_o = reinterpret_cast<uint16_t*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)a.n_q * a.n_split * a.H * a.D_v);
+  }
+  return from_hip(dsa::launch_dense_mqa(a, stream));
+}
+
+}  // namespace
+
+dsa_status dsa_dense_mqa_prefill(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
+                                 const int32_t* q_pos, int32_t n_q, int32_t H, int32_t D_k,
+                                 int32_t D_v, float scale, uint16_t* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n_q < 0 || n_kv < 1 || !isfinite(scale)) return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > kMaxH || !dsa::mqa_shape_supported(D_k, D_v)) return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (n_q > 0x7fffffff / 2 || !q || !kv || !q_pos || !out) return DSA_ERR_INVALID_ARG;
+  dsa::MqaArgs a{};
+  a.q = q; a.kv = kv; a.qpos_or_ctx = q_pos; a.n_kv = n_kv; a.n_q = n_q; a.H = H;
+  a.D_k = D_k; a.D_v = D_v; a.scale = scale; a.out = out; a.lse = lse;
+  return dense_launch(a, n_kv, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_dense_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
+                                const int32_t* page_table, const int32_t* ctx_lens, int32_t B,
+                                int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t H,
+                                int32_t D_k, int32_t D_v, float scale, uint16_t* out,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (B < 0 || !paging_ok(max_pages, n_pages, page_size) || !isfinite(scale))
+    return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > kMaxH || !dsa::mqa_shape_supported(D_k, D_v)) return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (B == 0) return DSA_OK;
+  if (B > 0x7fffffff / 2 || !q || !kv_cache || !page_table || !ctx_lens || !out)
+    return DSA_ERR_INVALID_ARG;
+  dsa::MqaArgs a{};
+  a.q = q; a.kv = kv_cache; a.qpos_or_ctx = ctx_lens; a.page_table = page_table;
+  a.max_pages = max_pages; a.n_pages = n_pages; a.page_size = page_size; a.n_q = B; a.H = H;
+  a.D_k = D_k; a.D_v = D_v; a.scale = scale; a.out = out; a.lse = lse;
+  return dense_launch(a, max_pages * page_size, workspace, workspace_bytes, stream);
+}
+
 dsa_status dsa_cache_append(const uint16_t* k_new, const uint16_t* kv_new, const int32_t* seq,
                             const int32_t* pos, const int32_t* page_table, int32_t T,
                             int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t d_I,

@@ -53,6 +53,10 @@ struct MqaArgs {
 };
 bool mqa_shape_supported(int D_k, int D_v);
 hipError_t launch_sparse_mqa(const MqaArgs& a, hipStream_t stream);
+// Dense causal attention over positions 0..t (idx unused); n_split / rows_per_split set by the
+// caller with rows_per_split = dense_rows_per_split().
+hipError_t launch_dense_mqa(const MqaArgs& a, hipStream_t stream);
+int dense_rows_per_split();
 
 // Bytes of the per-device static scratch array of the allocation-free decode entry point.
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;

@@ -194,7 +194,10 @@ __host__ __device__ constexpr int vm_wait_imm(int n) {
 // sequence qi with t = ctx[qi] - 1; in a batched prefill (n_seq > 0) row qi is sequence
 // q_seq[qi] (0 when q_seq is NULL; a sequence outside [0, n_seq) attends nothing) with
 // t = q_pos[qi].
-template <int DK, int DV, bool PAGED>
+// DENSE: the rows attended are all positions 0..t (dense causal attention, the baseline the
+// selection is measured against); split sp takes positions [sp * rows_per_split, ...), and
+// `idx` is not read.
+template <int DK, int DV, bool PAGED, bool DENSE>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ qpos_or_ctx,
@@ -241,7 +244,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   }
   const int r0 = sp * rows_per_split;
   int r1 = r0 + rows_per_split;
-  if (r1 > top_k) r1 = top_k;
+  const int n_list = DENSE ? t + 1 : top_k;   // entries of the row's list
+  if (r1 > n_list) r1 = n_list;
   const int nrows = r1 > r0 ? r1 - r0 : 0;
 
   // ---- queries: B operand of k-step ks = dims 32ks + 8g .. +8 of head `head` (issued first,
@@ -266,7 +270,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int i = tid + k * NT;
-      sv[k] = i < nrows ? idx[(size_t)qi * top_k + r0 + i] : -1;
+      if (DENSE) sv[k] = i < nrows ? r0 + i : -1;
+      else sv[k] = i < nrows ? idx[(size_t)qi * top_k + r0 + i] : -1;
     }
     int pg[RPT];
 #pragma unroll
@@ -488,12 +493,46 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 // its running max m_i and sum l_i, so o = sum_i w_i (o_i / l_i) / sum_i w_i with
 // w_i = exp2(m_i - M) l_i.  One workgroup per (query, head); each thread owns 4 consecutive dims
 // and issues the reads of every partial before using any (one memory round trip).
+// MAXS = 0: any number of partials, read in two passes (the maxima, then the weighted sum)
+// with no per-partial registers.
 template <int DV, int MAXS>
 __global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const uint16_t* __restrict__ part_o,
                                                              const float* __restrict__ part_ml,
                                                              int H, int n_split,
                                                              uint16_t* __restrict__ out,
                                                              float* __restrict__ lse) {
+  if constexpr (MAXS == 0) {
+    const int qi = blockIdx.x / H;
+    const int h = blockIdx.x - qi * H;
+    const size_t base = (size_t)qi * n_split * H + h;
+    const int d = 4 * threadIdx.x;
+    float M = -__builtin_inff();
+    for (int i = 0; i < n_split; ++i) M = fmaxf(M, part_ml[(base + (size_t)i * H) * 2]);
+    float L = 0.f;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -__builtin_inff()) {
+#pragma unroll 4
+      for (int i = 0; i < n_split; ++i) {
+        const size_t b = base + (size_t)i * H;
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + b * 2);
+        const uint2 ov = *reinterpret_cast<const uint2*>(part_o + b * DV + d);
+        const float wgt = exp2f(ml.x - M) * ml.y;
+        L += wgt;
+        acc[0] += wgt * bf16_to_f32((uint16_t)(ov.x & 0xffffu));
+        acc[1] += wgt * bf16_to_f32((uint16_t)(ov.x >> 16));
+        acc[2] += wgt * bf16_to_f32((uint16_t)(ov.y & 0xffffu));
+        acc[3] += wgt * bf16_to_f32((uint16_t)(ov.y >> 16));
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 o;
+    o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<uint2*>(out + ((size_t)qi * H + h) * DV + d) = o;
+    if (lse != nullptr && threadIdx.x == 0)
+      lse[(size_t)qi * H + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -__builtin_inff();
+    return;
+  } else {
   const int qi = blockIdx.x / H;
   const int h = blockIdx.x - qi * H;
   const size_t base = (size_t)qi * n_split * H + h;   // partial i lives at base + i*H
@@ -537,32 +576,58 @@ __global__ __launch_bounds__(DV / 4) void mqa_combine_kernel(const uint16_t* __r
   *reinterpret_cast<uint2*>(out + ((size_t)qi * H + h) * DV + d) = o;
   if (lse != nullptr && threadIdx.x == 0)
     lse[(size_t)qi * H + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -__builtin_inff();
+  }
+}
+
+template <int DV>
+hipError_t launch_combine(const MqaArgs& a, hipStream_t stream) {
+  if (a.n_split <= 4)
+    hipLaunchKernelGGL((mqa_combine_kernel<DV, 4>), dim3(a.n_q * a.H), dim3(DV / 4), 0, stream,
+                       a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
+  else
+    hipLaunchKernelGGL((mqa_combine_kernel<DV, 0>), dim3(a.n_q * a.H), dim3(DV / 4), 0, stream,
+                       a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
+  return hipGetLastError();
+}
+
+// Dense causal attention (every position 0..t): split over workgroups of up to MAX_ROWS
+// positions, merged by the combine kernel.
+template <int DK, int DV>
+hipError_t launch_dense_shape(const MqaArgs& a, hipStream_t stream) {
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  const int rps = a.rows_per_split;
+  if (a.page_table == nullptr)
+    hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, true>), dim3(a.n_q, a.n_split),
+                       dim3(NT), 0, stream, a.q, a.kv, nullptr, a.qpos_or_ctx, nullptr, nullptr,
+                       0, 0, 0, 1, a.n_kv, a.H, 0, scale_log2, a.n_split, rps, a.out, a.lse,
+                       a.part_o, a.part_ml);
+  else
+    hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true, true>), dim3(a.n_q, a.n_split),
+                       dim3(NT), 0, stream, a.q, a.kv, nullptr, a.qpos_or_ctx, a.page_table,
+                       nullptr, 0, a.max_pages, a.n_pages, a.page_size, 0, a.H, 0, scale_log2,
+                       a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  return launch_combine<DV>(a, stream);
 }
 
 template <int DK, int DV>
 hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   if (a.page_table == nullptr) {
-    hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false>), dim3(a.n_q, 1), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, false>), dim3(a.n_q, 1), dim3(NT), 0, stream,
                        a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0, 0, 1, a.n_kv,
                        a.H, a.top_k, scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr);
     return hipGetLastError();
   }
   const int rps = a.rows_per_split;
-  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true>), dim3(a.n_q, a.n_split), dim3(NT), 0,
+  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true, false>), dim3(a.n_q, a.n_split), dim3(NT), 0,
                      stream, a.q, a.kv, a.idx, a.qpos_or_ctx, a.page_table, a.q_seq, a.n_seq,
                      a.max_pages, a.n_pages, a.page_size, 0, a.H, a.top_k, scale_log2,
                      a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  // partial counts up to the ABI's limit of 16 splits
-  if (a.n_split <= 4)
-    hipLaunchKernelGGL((mqa_combine_kernel<DV, 4>), dim3(a.n_q * a.H), dim3(DV / 4), 0, stream,
-                       a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
-  else
-    hipLaunchKernelGGL((mqa_combine_kernel<DV, 16>), dim3(a.n_q * a.H), dim3(DV / 4), 0,
-                       stream, a.part_o, a.part_ml, a.H, a.n_split, a.out, a.lse);
-  return hipGetLastError();
+  return launch_combine<DV>(a, stream);
 }
 
 }  // namespace
@@ -608,5 +673,14 @@ hipError_t launch_sparse_mqa(const MqaArgs& a, hipStream_t stream) {
   if (a.D_k == 96 && a.D_v == 64) return launch_shape<96, 64>(a, stream);
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_dense_mqa(const MqaArgs& a, hipStream_t stream) {
+  if (a.D_k == 576 && a.D_v == 512) return launch_dense_shape<576, 512>(a, stream);
+  if (a.D_k == 64 && a.D_v == 64) return launch_dense_shape<64, 64>(a, stream);
+  if (a.D_k == 96 && a.D_v == 64) return launch_dense_shape<96, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+int dense_rows_per_split() { return MAX_ROWS; }
 
 }  // namespace dsa

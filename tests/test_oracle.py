@@ -369,6 +369,44 @@ def test_cache_append_writes_the_slots_and_nothing_else():
         k_new.float().clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)))
 
 
+# --------------------------------------------------------------------------- dense baseline
+
+@pytest.mark.parametrize("D_k,D_v", [(64, 64), (96, 64)])
+def test_dense_prefill_equals_causal_sdpa(D_k, D_v):
+    """The dense baseline is torch's causal scaled_dot_product_attention (fp64, CPU) with every
+    head reading the one shared row (K = the row, V = its first D_v dims)."""
+    wl = gi.Workload(name="d", L=90, idx=gi.IndexerSpec(H_I=4, d_I=32, top_k=8),
+                     mqa=gi.MqaSpec(H=3, D_k=D_k, D_v=D_v, sigma=1.0, scale=D_k ** -0.5), seed=4)
+    d = gi.prefill_inputs(wl)
+    o, lse = orc.dense_prefill(d)
+    q = d["q"].double().permute(1, 0, 2)                      # [H, L, D_k]
+    kv = d["kv"].double()
+    k = kv[None].expand(3, -1, -1)
+    v = kv[None, :, :D_v].expand(3, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                                           scale=D_k ** -0.5)
+    assert np.allclose(o, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    z = (q @ k.transpose(1, 2)) * D_k ** -0.5
+    z = z.masked_fill(torch.triu(torch.ones(90, 90, dtype=torch.bool), 1), float("-inf"))
+    assert np.allclose(lse, torch.logsumexp(z, -1).T.numpy(), rtol=0, atol=1e-12)
+
+
+def test_dense_decode_equals_dense_prefill_last_row():
+    sp = gi.DecodeSpec(B=2, idx=gi.IndexerSpec(H_I=4, d_I=32, top_k=8),
+                       mqa=gi.MqaSpec(H=2, D_k=64, D_v=64, sigma=1.0, scale=0.125), seed=6)
+    d = gi.decode_inputs(sp, ctx_lens=(150, 77))
+    o, lse = orc.dense_decode(d)
+    P = d["page_size"]
+    for b, n in enumerate(d["ctx"].tolist()):
+        s = torch.arange(n)
+        pages = d["page_table"][b][s // P].long()
+        pre = {"q": d["q"][b:b + 1], "kv": d["kv_cache"][pages, s % P], "D_v": 64,
+               "scale": 0.125, "q_pos": torch.tensor([n - 1])}
+        o2, l2 = orc.dense_prefill(pre)
+        assert np.allclose(o[b], o2[0], rtol=0, atol=1e-13)
+        assert np.allclose(lse[b], l2[0], rtol=0, atol=1e-13)
+
+
 # --------------------------------------------------------------------------- batched prefill
 
 def _contiguous_of(d, b, rows):
