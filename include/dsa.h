@@ -250,6 +250,33 @@ dsa_status dsa_dense_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
                                 hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * The indexer's training signal: KL divergence from the main attention's distribution to the
+ * indexer's (the indexer is trained to reproduce how the main attention distributes itself,
+ * with a KL-divergence loss: jdon.com "DeepSeek-V3.2-Exp" article, paragraph on the indexer's
+ * warm-up; in the sparse stage the indexer's loss stays separate from the model's).  Forward
+ * and the gradient with respect to the indexer scores, over each row's index list S (entries
+ * that are -1 or outside [0, t] are not part of it; for the dense warm-up pass every position
+ * as the list):
+ *   target[t,e] = (1/H) sum_h softmax_S(scale q[t,h] . kv[s])[e]    (main attention)
+ *   q_I[t,e]    = softmax_S(I[t, idx[t,e]])                          (indexer)
+ *   loss[t]     = sum_e target (log target - log q_I),   grad[t,e] = q_I - target
+ *
+ * q [n_q, H, D_k] bf16, kv [n_kv, D_k] bf16, idx [n_q, top_k], q_pos [n_q], lse [n_q, H] fp32:
+ * the forward's log-sum-exp over the same lists (dsa_sparse_mqa_prefill's lse output);
+ * q_idx [n_q, H_I, d_I] FP8, w [n_q, H_I], k_idx [n_kv, d_I] FP8 (the indexer's inputs);
+ * outputs (device, fp32): target [n_q, top_k] (0 for entries outside S), loss [n_q]
+ * (0 for an empty list), grad [n_q, top_k] or NULL (0 outside S).  D_k in {576, 64, 96}.
+ * The logits are recomputed with bf16 MFMAs and fp32 accumulation as in the forward; the
+ * indexer scores are recomputed as the decode scorer forms them.
+ * ------------------------------------------------------------------------------------- */
+dsa_status dsa_indexer_kl(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
+                          const int32_t* idx, const int32_t* q_pos, const float* lse,
+                          int32_t n_q, int32_t H, int32_t D_k, int32_t top_k, float scale,
+                          const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                          int32_t H_I, int32_t d_I, float* target, float* loss, float* grad,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Cache write: append new tokens to the paged caches the decode calls read.  Defines the step
  * just before the paged indexer and attention: the indexer keeps its keys in FP8 (jdon.com
  * "DeepSeek-V3.2-Exp" article, paragraph on the lightning indexer) in 64-token pages

@@ -269,6 +269,59 @@ def decode(inp: dict, seqs=None, idx=None):
     return out_idx, o, lse
 
 
+def kl_from_scores(scores: np.ndarray, target: np.ndarray):
+    """(loss, grad) of the indexer's KL loss for one row, over the entries of its list:
+    loss = sum_e target[e] (log target[e] - log softmax(scores)[e]) (0 log 0 = 0), and
+    grad[e] = d loss / d scores[e] = softmax(scores)[e] - target[e] (target sums to 1).
+    Empty list: (0, [])."""
+    if scores.shape[0] == 0:
+        return 0.0, np.zeros(0)
+    m = scores.max()
+    log_q = scores - m - np.log(np.exp(scores - m).sum())
+    pos = target > 0
+    loss = float((target[pos] * (np.log(target[pos]) - log_q[pos])).sum())
+    return loss, np.exp(log_q) - target
+
+
+def indexer_kl(inp: dict, idx, rows=None):
+    """The indexer's training signal for the given rows and index lists (one contiguous
+    sequence): the main attention's probabilities over the row's list, summed over heads and
+    divided by H, are the target; the indexer's distribution is the softmax of its scores over
+    the same list; the loss is their KL divergence, target first.  The indexer learns to
+    reproduce the main attention with a KL loss (jdon.com article, paragraph on the indexer's
+    warm-up; its sparse-training paragraph keeps that loss separate from the model's).
+    Returns (loss [n], target [n, k], grad [n, k]); entries outside [0, t] or -1 are not in the
+    list (target and grad 0 there).
+    """
+    q_pos = _np(inp["q_pos"]).astype(np.int64)
+    rows = list(range(q_pos.shape[0])) if rows is None else list(rows)
+    idx = np.asarray(idx)
+    k = idx.shape[1]
+    kv = _np(inp["kv"])
+    k_i = decode_e4m3fn(inp["k_idx"])
+    q_codes = _np(inp["q_idx"])
+    w = _np(inp["w"]).astype(np.float64)
+    scale = float(inp["scale"])
+    loss = np.zeros(len(rows))
+    target = np.zeros((len(rows), k))
+    grad = np.zeros((len(rows), k))
+    for r, i in enumerate(rows):
+        t = min(int(q_pos[i]), kv.shape[0] - 1)
+        listed = np.flatnonzero((idx[r] >= 0) & (idx[r] <= t))
+        if listed.size == 0:
+            continue
+        s = idx[r][listed]
+        z = scale * (decode_bf16(inp["q"][i]) @ decode_bf16(kv[s]).T)       # [H, m] logits
+        a = np.exp(z - z.max(axis=1, keepdims=True))
+        a /= a.sum(axis=1, keepdims=True)                                   # per-head softmax
+        p = a.mean(axis=0)                                                  # heads summed / H
+        sc = indexer_scores(decode_e4m3fn(q_codes[i]), w[i], k_i)[s]
+        loss[r], g = kl_from_scores(sc, p)
+        target[r, listed] = p
+        grad[r, listed] = g
+    return loss, target, grad
+
+
 def dense_prefill(inp: dict, rows=None):
     """Dense causal attention, the baseline DSA replaces: row t attends every position 0..t
     (t = q_pos, clamped to the KV rows; t < 0 attends nothing).  Returns (o [n,H,D_v],
@@ -450,7 +503,8 @@ def selected_pairs(L: int, k: int) -> int:
 __all__ = [
     "E4M3FN", "decode_e4m3fn", "decode_bf16", "indexer_scores", "topk_select", "sparse_mqa",
     "valid_selected", "prefill_indexer_topk", "prefill", "paged_gather", "paged_rows", "decode",
-    "batched_prefill", "dense_prefill", "dense_decode", "quantize_e4m3fn", "cache_append",
+    "batched_prefill", "dense_prefill", "dense_decode", "kl_from_scores", "indexer_kl",
+    "quantize_e4m3fn", "cache_append",
     "row_work",
     "causal_pairs", "selected_pairs",
 ]

@@ -51,6 +51,8 @@ SIGNATURES = {
                                              _P]),
     "dsa_dense_mqa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P,
                                             _P, _P, _Z, _P]),
+    "dsa_indexer_kl": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _I,
+                                      _I, _P, _P, _P, _P]),
     "dsa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dsa_sparse_mqa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                      _I, _I, _I, _F, _I, _P, _P, _P]),
@@ -392,6 +394,35 @@ def dense_mqa_decode(q, kv_cache, page_table, ctx_lens, d_v: int, scale: float, 
     return out, lse
 
 
+def indexer_kl(q, kv, idx, q_pos, lse, scale: float, q_idx, w, k_idx, want_grad: bool = True):
+    """The indexer's training signal (dsa_indexer_kl): returns (loss [n_q], target [n_q, top_k],
+    grad [n_q, top_k] or None) for the index lists idx, given the forward's lse."""
+    lib = load_library()
+    _need(q, "q", _BF16, 3)
+    dev = q.device
+    n_q, H, D_k = q.shape
+    top_k = idx.shape[1] if isinstance(idx, torch.Tensor) else 0
+    _need(kv, "kv", _BF16, 2, dev)
+    _need(idx, "idx", _I32, 2, dev, shape=(n_q, top_k))
+    _need(q_pos, "q_pos", _I32, 1, dev, shape=(n_q,))
+    _need(lse, "lse", _F32, 2, dev, shape=(n_q, H))
+    _need(q_idx, "q_idx", _FP8, 3, dev)
+    H_I, d_I = q_idx.shape[1], q_idx.shape[2]
+    _need(q_idx, "q_idx", _FP8, 3, dev, shape=(n_q, H_I, d_I))
+    _need(w, "w", _F32, 2, dev, shape=(n_q, H_I))
+    _need(k_idx, "k_idx", _FP8, 2, dev, shape=(kv.shape[0], d_I))
+    if kv.shape[1] != D_k:
+        raise ValueError("kv rows do not match q")
+    target = torch.empty((n_q, top_k), dtype=torch.float32, device=dev)
+    loss = torch.empty((n_q,), dtype=torch.float32, device=dev)
+    grad = torch.empty((n_q, top_k), dtype=torch.float32, device=dev) if want_grad else None
+    _check(lib.dsa_indexer_kl(_ptr(q), _ptr(kv), kv.shape[0], _ptr(idx), _ptr(q_pos), _ptr(lse),
+                              n_q, H, D_k, top_k, float(scale), _ptr(q_idx), _ptr(w), _ptr(k_idx),
+                              H_I, d_I, _ptr(target), _ptr(loss), _ptr(grad), _stream(dev)),
+           "dsa_indexer_kl")
+    return loss, target, grad
+
+
 def cache_append(page_table, pos, k_cache=None, kv_cache=None, k_new=None, kv_new=None,
                  seq=None):
     """Append new tokens to the paged caches (dsa_cache_append): k_new [T, d_I] bf16 is
@@ -474,7 +505,7 @@ def sparse_mqa_decode_noalloc(q, kv_cache, page_table, ctx_lens, idx, d_v: int, 
 __all__ = ["load_library", "DSAError", "indexer_topk", "indexer_topk_paged",
            "sparse_mqa_prefill", "sparse_mqa_decode", "sparse_mqa_decode_noalloc", "cache_append",
            "indexer_topk_batched", "sparse_mqa_batched", "dense_mqa_prefill",
-           "dense_mqa_decode", "dense_mqa_workspace_size",
+           "dense_mqa_decode", "dense_mqa_workspace_size", "indexer_kl",
            "indexer_topk_workspace_size",
            "indexer_topk_paged_workspace_size", "sparse_mqa_decode_workspace_size",
            "SIGNATURES", "LIB_PATH"]

@@ -230,6 +230,30 @@ dsa_status dsa_dense_mqa_decode(const uint16_t* q, const uint16_t* kv_cache,
   return dense_launch(a, max_pages * page_size, workspace, workspace_bytes, stream);
 }
 
+dsa_status dsa_indexer_kl(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
+                          const int32_t* idx, const int32_t* q_pos, const float* lse,
+                          int32_t n_q, int32_t H, int32_t D_k, int32_t top_k, float scale,
+                          const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                          int32_t H_I, int32_t d_I, float* target, float* loss, float* grad,
+                          hipStream_t stream) {
+  if (n_q < 0 || n_kv < 1 || !isfinite(scale)) return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > kMaxH || !(D_k == 576 || D_k == 64 || D_k == 96) ||
+      !indexer_shape_ok(H_I, d_I, top_k))
+    return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (n_q > 0x7fffffff / 2 || !q || !kv || !idx || !q_pos || !lse || !q_idx || !w || !k_idx ||
+      !target || !loss)
+    return DSA_ERR_INVALID_ARG;
+  dsa::MqaArgs a{};
+  a.q = q; a.kv = kv; a.idx = idx; a.qpos_or_ctx = q_pos; a.n_kv = n_kv; a.n_q = n_q; a.H = H;
+  a.D_k = D_k; a.D_v = D_k == 576 ? 512 : 64; a.top_k = top_k; a.scale = scale;
+  a.n_split = 1; a.rows_per_split = top_k;
+  hipError_t e = dsa::launch_mqa_probs(a, lse, target, stream);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  return from_hip(dsa::launch_indexer_kl(q_idx, w, k_idx, n_kv, q_pos, idx, n_q, top_k, H_I, d_I,
+                                         target, loss, grad, stream));
+}
+
 dsa_status dsa_cache_append(const uint16_t* k_new, const uint16_t* kv_new, const int32_t* seq,
                             const int32_t* pos, const int32_t* page_table, int32_t T,
                             int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t d_I,

@@ -21,6 +21,10 @@ hipError_t launch_indexer_topk_batched(const uint8_t* q_idx, const float* w,
                                        const int32_t* q_seq, const int32_t* q_pos, int n_q,
                                        int H_I, int d_I, int top_k, int32_t* out_idx, void* ws,
                                        hipStream_t stream);
+hipError_t launch_indexer_kl(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                             int n_keys, const int32_t* q_pos, const int32_t* idx, int n_q,
+                             int top_k, int H_I, int d_I, const float* target, float* loss,
+                             float* grad, hipStream_t stream);
 hipError_t launch_indexer_topk_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_cache,
                                      const int32_t* page_table, const int32_t* ctx_lens, int B,
                                      int max_pages, int n_pages, int page_size, int H_I, int d_I,
@@ -57,6 +61,10 @@ hipError_t launch_sparse_mqa(const MqaArgs& a, hipStream_t stream);
 // caller with rows_per_split = dense_rows_per_split().
 hipError_t launch_dense_mqa(const MqaArgs& a, hipStream_t stream);
 int dense_rows_per_split();
+// Main-attention probabilities of each listed entry, summed over heads and divided by H
+// (contiguous rows, n_split = 1), from the forward's natural-log lse.
+hipError_t launch_mqa_probs(const MqaArgs& a, const float* lse_in, float* probs,
+                            hipStream_t stream);
 
 // Bytes of the per-device static scratch array of the allocation-free decode entry point.
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;

@@ -1330,11 +1330,120 @@ __global__ __launch_bounds__(SEL_NT) void dec_finish_kernel(const int32_t* __res
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Indexer training signal (KL to the main attention), one workgroup per query row.
+// The indexer is trained to reproduce the main attention's distribution with a KL-divergence
+// loss (jdon.com "DeepSeek-V3.2-Exp" article, paragraph on the indexer's warm-up; in the
+// sparse stage the indexer keeps its own loss, separate from the language-model gradients).
+// Over the row's index list S (entries -1 or outside [0, t] are not part of it):
+//   p[e] = target[e]                       main attention, summed over heads, / H (given)
+//   q[e] = softmax_e(I[t, idx[e]])         the indexer's scores of the listed keys
+//   loss = sum_e p[e] (log p[e] - log q[e]),  grad[e] = d loss / d I = q[e] - p[e]
+// The scores are recomputed exactly as the decode scorer forms them (fp32 fma of
+// w * max(x, 0) over the FP8 MFMA head products), so on a dyadic grid they are exact.
+// ------------------------------------------------------------------------------------------
+constexpr int KL_NT = 256;
+constexpr int KL_WAVES = KL_NT / kWave;
+
+__global__ __launch_bounds__(KL_NT) void indexer_kl_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, int n_keys, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ idx, int top_k, int H_I, int d_I,
+    const float* __restrict__ target, float* __restrict__ loss, float* __restrict__ grad) {
+  __shared__ float sc[kMaxK];
+  __shared__ float red[KL_WAVES];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t = min(q_pos[row], n_keys - 1);
+  // A operand: the row's heads 16 hg + c16; weights of output rows 4g + i
+  v8i qa[4];
+  float wl[4][4];
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) {
+    const int h = 16 * hg + c16;
+    qa[hg] = load_row32(q_idx + ((size_t)row * H_I + (h < H_I ? h : 0)) * d_I, g, d_I, h < H_I);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * hg + 4 * g + i;
+      wl[hg][i] = hh < H_I ? w[(size_t)row * H_I + hh] : 0.f;
+    }
+  }
+  const int n_frag = (top_k + 15) / 16;
+  for (int f = wave; f < n_frag; f += KL_WAVES) {
+    const int e = 16 * f + c16;
+    const int s = e < top_k ? idx[(size_t)row * top_k + e] : -1;
+    const bool ok = s >= 0 && s <= t;
+    const v8i kf = load_row32(k_idx + (size_t)(ok ? s : 0) * d_I, g, d_I, ok);
+    float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      if (16 * hg >= H_I) break;
+      const v4f x = mfma_fp8(qa[hg], kf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a4[i] = fmaf(wl[hg][i], fmaxf(x[i], 0.f), a4[i]);
+    }
+    float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    if (g == 0 && e < top_k) sc[e] = ok ? acc : -__builtin_inff();
+  }
+  __syncthreads();
+  // softmax of the listed scores
+  float m = -__builtin_inff();
+  for (int e = tid; e < top_k; e += KL_NT) m = fmaxf(m, sc[e]);
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int v = 1; v < KL_WAVES; ++v) m = fmaxf(m, red[v]);
+  __syncthreads();
+  float z = 0.f;
+  if (m != -__builtin_inff())
+    for (int e = tid; e < top_k; e += KL_NT) z += expf(sc[e] - m);
+  for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+  if (lane == 0) red[wave] = z;
+  __syncthreads();
+  z = 0.f;
+#pragma unroll
+  for (int v = 0; v < KL_WAVES; ++v) z += red[v];
+  __syncthreads();
+  const float log_z = logf(z);
+  float kl = 0.f;
+  for (int e = tid; e < top_k; e += KL_NT) {
+    const float p = target[(size_t)row * top_k + e];
+    const bool listed = sc[e] != -__builtin_inff();
+    const float log_q = sc[e] - m - log_z;
+    if (listed && p > 0.f) kl += p * (logf(p) - log_q);
+    if (grad != nullptr)
+      grad[(size_t)row * top_k + e] = listed ? expf(log_q) - p : 0.f;
+  }
+  for (int o = 32; o >= 1; o >>= 1) kl += __shfl_xor(kl, o);
+  if (lane == 0) red[wave] = kl;
+  __syncthreads();
+  if (tid == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int v = 0; v < KL_WAVES; ++v) tot += red[v];
+    loss[row] = m == -__builtin_inff() ? 0.f : tot;
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------
 // Host launchers
 // ------------------------------------------------------------------------------------------
+hipError_t launch_indexer_kl(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                             int n_keys, const int32_t* q_pos, const int32_t* idx, int n_q,
+                             int top_k, int H_I, int d_I, const float* target, float* loss,
+                             float* grad, hipStream_t stream) {
+  hipLaunchKernelGGL(indexer_kl_kernel, dim3(n_q), dim3(KL_NT), 0, stream, q_idx, w, k_idx,
+                     n_keys, q_pos, idx, top_k, H_I, d_I, target, loss, grad);
+  return hipGetLastError();
+}
+
 int indexer_cap(int top_k) {
   // room for top_k kept items plus at least two iterations of appends
   int cap = 2 * top_k + BK2;

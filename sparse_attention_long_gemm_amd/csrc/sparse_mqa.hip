@@ -197,7 +197,11 @@ __host__ __device__ constexpr int vm_wait_imm(int n) {
 // DENSE: the rows attended are all positions 0..t (dense causal attention, the baseline the
 // selection is measured against); split sp takes positions [sp * rows_per_split, ...), and
 // `idx` is not read.
-template <int DK, int DV, bool PAGED, bool DENSE>
+// PROBS: no attention output; instead, for every entry of the row's index list, the main
+// attention's probability summed over the heads and divided by H, from the logits recomputed
+// here and the forward's log-sum-exp `lse` (read, natural log): probs[qi, e] =
+// (1/H) sum_h exp(scale q_h . kv_s - lse_h), 0 for an entry that is not attended.
+template <int DK, int DV, bool PAGED, bool DENSE, bool PROBS = false>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ qpos_or_ctx,
@@ -205,14 +209,16 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     int max_pages, int n_pages, int page_size, int n_kv,
     int H, int top_k, float scale_log2, int n_split, int rows_per_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, float* __restrict__ probs) {
   static_assert(DK % 32 == 0 && DV % 16 == 0 && DV <= DK, "shape");
+  static_assert(!(PROBS && (PAGED || DENSE)), "probabilities: contiguous sparse rows only");
   using Sh = MqaShared;
   constexpr int NKS = DK / 32;           // k-steps of the S^T product
   constexpr int NDB = DV / 16;           // 16-dim blocks of the output
   constexpr int RS = Tile<DK>::RS;
   constexpr int GJ = Tile<DK>::GJ;
   __shared__ Sh sh;
+  __shared__ float psh[2][CH];   // PROBS: head sums of the current / previous chunk
   __shared__ __attribute__((aligned(16))) uint8_t kt0[Tile<DK>::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t kt1[Tile<DK>::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t kt2[Tile<DK>::BYTES];
@@ -312,6 +318,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   const int my_loads = gather_count<DK>(wave) * gather_insts<DK>();
   int slot_off[GJ];
   gather_plan<DK>(wave, lane, slot_off);
+  if (PROBS && tid < 2 * CH) psh[tid / CH][tid % CH] = 0.f;
   __syncthreads();   // rows[] complete
   int row_nx = chunk_row(0);
   if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane, 0, GJ, slot_off);
@@ -339,9 +346,25 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   const int tq = lane & 3, tm = (lane & 15) >> 2;
   const int tr_off = (4 * g + tm) * RS + 8 * tq;
 
+  // PROBS: this lane's head's log-sum-exp in log2 units; the chunk sums are written out one
+  // step later by wave 0 (the barrier at the end of each step separates the two buffers' uses)
+  float lse2 = 0.f;
+  if constexpr (PROBS) lse2 = head_ok ? lse[(size_t)qi * H + head] * 1.4426950408889634f : 0.f;
+  const float inv_h = 1.f / (float)H;
+  auto flush_probs = [&](int cc) {
+    if (wave == 0 && lane < CH) {
+      const int e = cc * CH + lane;
+      if (e < nrows) probs[(size_t)qi * top_k + r0 + e] = psh[cc & 1][lane] * inv_h;
+      psh[cc & 1][lane] = 0.f;
+    }
+  };
+
   auto step = [&](const lds_u8* tile, uint8_t* gtile, int c) {
     const bool more = c + 2 < n_chunks;    // chunk c+2 is gathered during this step
     const u32 vmask = vm_a;
+    if constexpr (PROBS) {
+      if (c >= 1) flush_probs(c - 1);
+    }
 
     // ---- S^T = K Q^T: 32 keys (two blocks of 16) x this wave's 16 heads ----
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -366,6 +389,26 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    if constexpr (PROBS) {
+      // probabilities of this lane's 8 keys for its head, summed over the wave's 16 heads
+      const u32 vmp = vmask >> (4 * g);
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = i < 4 ? s0[i & 3] : s1[i & 3];
+        const bool ok = head_ok && ((vmp >> ((i < 4 ? 0 : 16) + (i & 3))) & 1u);
+        pv[i] = ok ? __builtin_amdgcn_exp2f(fmaf(x, scale_log2, -lse2)) : 0.f;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] += __shfl_xor(pv[i], o);
+      if (h16 == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          atomicAdd(&psh[c & 1][(i < 4 ? 0 : 16) + 4 * g + (i & 3)], pv[i]);
+      }
+    } else {
     // ---- online softmax: lane holds keys 4g + i (s0) and 16 + 4g + i (s1) of head h16 ----
     const u32 vml = vmask >> (4 * g);   // bit i: key 4g + i; bit 16 + i: key 16 + 4g + i
     float psum = 0.f;
@@ -433,6 +476,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       o[d] = mfma16_bf16(a, pb, o[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    }   // !PROBS
     vm_a = vm_b;
     vm_b = (u32)wave_ballot(row_nx >= 0);
     row_nx = chunk_row(c + 3);
@@ -451,6 +495,11 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     step((const lds_u8*)kt0, kt2, c);
     if (c + 1 < n_chunks) step((const lds_u8*)kt1, kt0, c + 1);
     if (c + 2 < n_chunks) step((const lds_u8*)kt2, kt1, c + 2);
+  }
+
+  if constexpr (PROBS) {
+    if (n_chunks > 0) flush_probs(n_chunks - 1);   // after the last step's barrier
+    return;
   }
 
   // ---- epilogue: lane holds head `head`, dims 16d + 4g + i ----
@@ -600,12 +649,12 @@ hipError_t launch_dense_shape(const MqaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, true>), dim3(a.n_q, a.n_split),
                        dim3(NT), 0, stream, a.q, a.kv, nullptr, a.qpos_or_ctx, nullptr, nullptr,
                        0, 0, 0, 1, a.n_kv, a.H, 0, scale_log2, a.n_split, rps, a.out, a.lse,
-                       a.part_o, a.part_ml);
+                       a.part_o, a.part_ml, nullptr);
   else
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true, true>), dim3(a.n_q, a.n_split),
                        dim3(NT), 0, stream, a.q, a.kv, nullptr, a.qpos_or_ctx, a.page_table,
                        nullptr, 0, a.max_pages, a.n_pages, a.page_size, 0, a.H, 0, scale_log2,
-                       a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml);
+                       a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   return launch_combine<DV>(a, stream);
@@ -617,14 +666,15 @@ hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
   if (a.page_table == nullptr) {
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, false>), dim3(a.n_q, 1), dim3(NT), 0, stream,
                        a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0, 0, 1, a.n_kv,
-                       a.H, a.top_k, scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr);
+                       a.H, a.top_k, scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr,
+                       nullptr);
     return hipGetLastError();
   }
   const int rps = a.rows_per_split;
   hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true, false>), dim3(a.n_q, a.n_split), dim3(NT), 0,
                      stream, a.q, a.kv, a.idx, a.qpos_or_ctx, a.page_table, a.q_seq, a.n_seq,
                      a.max_pages, a.n_pages, a.page_size, 0, a.H, a.top_k, scale_log2,
-                     a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml);
+                     a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   return launch_combine<DV>(a, stream);
@@ -682,5 +732,24 @@ hipError_t launch_dense_mqa(const MqaArgs& a, hipStream_t stream) {
 }
 
 int dense_rows_per_split() { return MAX_ROWS; }
+
+template <int DK, int DV>
+hipError_t launch_probs_shape(const MqaArgs& a, const float* lse_in, float* probs,
+                              hipStream_t stream) {
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, false, true>), dim3(a.n_q, 1), dim3(NT),
+                     0, stream, a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0, 0, 1,
+                     a.n_kv, a.H, a.top_k, scale_log2, 1, a.top_k, nullptr,
+                     const_cast<float*>(lse_in), nullptr, nullptr, probs);
+  return hipGetLastError();
+}
+
+hipError_t launch_mqa_probs(const MqaArgs& a, const float* lse_in, float* probs,
+                            hipStream_t stream) {
+  if (a.D_k == 576) return launch_probs_shape<576, 512>(a, lse_in, probs, stream);
+  if (a.D_k == 64) return launch_probs_shape<64, 64>(a, lse_in, probs, stream);
+  if (a.D_k == 96) return launch_probs_shape<96, 64>(a, lse_in, probs, stream);
+  return hipErrorInvalidValue;
+}
 
 }  // namespace dsa

@@ -407,6 +407,57 @@ def test_dense_decode_equals_dense_prefill_last_row():
         assert np.allclose(lse[b], l2[0], rtol=0, atol=1e-13)
 
 
+# --------------------------------------------------------------------------- indexer KL
+
+def test_kl_matches_torch_kl_div_and_is_zero_at_the_target():
+    g = torch.Generator().manual_seed(11)
+    sc = torch.randn(300, generator=g, dtype=torch.float64) * 3
+    tgt = torch.softmax(torch.randn(300, generator=g, dtype=torch.float64) * 2, 0)
+    tgt[:7] = 0
+    tgt /= tgt.sum()
+    loss, grad = orc.kl_from_scores(sc.numpy(), tgt.numpy())
+    ref = torch.nn.functional.kl_div(torch.log_softmax(sc, 0), tgt, reduction="sum")
+    assert abs(loss - ref.item()) <= 1e-12 * max(1.0, abs(ref.item()))
+    assert loss > 0
+    # scores equal to log(target) + c (target > 0 everywhere): the indexer matches, loss 0
+    t2 = torch.softmax(sc, 0).numpy()
+    l0, g0 = orc.kl_from_scores(np.log(t2) + 4.0, t2)
+    assert abs(l0) <= 1e-12 and np.abs(g0).max() <= 1e-12
+
+
+def test_kl_gradient_equals_finite_differences():
+    g = torch.Generator().manual_seed(12)
+    sc = (torch.randn(40, generator=g, dtype=torch.float64) * 2).numpy()
+    tgt = torch.softmax(torch.randn(40, generator=g, dtype=torch.float64), 0).numpy()
+    _, grad = orc.kl_from_scores(sc, tgt)
+    h = 1e-6
+    num = np.array([(orc.kl_from_scores(sc + h * np.eye(40)[e], tgt)[0] -
+                     orc.kl_from_scores(sc - h * np.eye(40)[e], tgt)[0]) / (2 * h)
+                    for e in range(40)])
+    assert np.abs(num - grad).max() <= 1e-7
+
+
+def test_indexer_kl_target_is_the_head_mean_of_softmax():
+    """The target of a row is the mean over heads of torch's softmax of the scaled logits over
+    the listed rows; it sums to 1; entries not in the list (-1, > t) get nothing."""
+    wl = gi.Workload(name="kl", L=120, idx=gi.IndexerSpec(H_I=4, d_I=32, top_k=24),
+                     mqa=gi.MqaSpec(H=5, D_k=64, D_v=64, sigma=1.0, scale=0.125), seed=8)
+    d = gi.prefill_inputs(wl)
+    idx = orc.prefill_indexer_topk(d)
+    idx[100, 3] = -1
+    idx[100, 4] = 119           # beyond t = 100: not in the list
+    loss, target, grad = orc.indexer_kl(d, idx, rows=None)
+    for t in (5, 30, 100, 119):
+        lst = [(e, s) for e, s in enumerate(idx[t]) if 0 <= s <= t]
+        s = torch.tensor([x for _, x in lst])
+        z = d["q"][t].double() @ d["kv"][s].double().T * 0.125
+        ref = torch.softmax(z, dim=1).mean(0).numpy()
+        assert np.allclose(target[t, [e for e, _ in lst]], ref, rtol=0, atol=1e-14)
+        assert abs(target[t].sum() - 1.0) <= 1e-12
+        assert loss[t] >= 0
+    assert target[100, 3] == 0 and target[100, 4] == 0 and grad[100, 4] == 0
+
+
 # --------------------------------------------------------------------------- batched prefill
 
 def _contiguous_of(d, b, rows):
