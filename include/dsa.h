@@ -277,6 +277,31 @@ dsa_status dsa_indexer_kl(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Sparse MQA backward: the gradients of sum(d_out * out) with respect to q and the KV rows,
+ * for the attention of dsa_sparse_mqa_prefill (the main model's loss in the sparse training
+ * stage flows through the selected entries only: jdon.com "DeepSeek-V3.2-Exp" article,
+ * sparse-training paragraph; MQA on the shared rows: openi.cn page, MLA/MQA item).  Per row t
+ * and head h over the listed entries (the selection is not differentiated):
+ *   P = exp(scale q.kv - lse), dP = d_out . v, dS = P (dP - sum_d d_out out),
+ *   d_q[t,h]     = scale sum_e dS kv_e                       (written, fp32 [n_q, H, D_k])
+ *   d_kv[s_e]   += scale sum_h dS q[t,h] + sum_h P d_out[t,h] (fp32 [n_kv, D_k], V part in the
+ *                                                              first D_v dims; ACCUMULATED:
+ *                                                              zero it before the first call)
+ * q, kv, idx, q_pos as in dsa_sparse_mqa_prefill; out [n_q, H, D_v] bf16 and lse [n_q, H]
+ * fp32 are that call's outputs; d_out [n_q, H, D_v] bf16.  workspace: P and dS in bf16,
+ * dsa_sparse_mqa_backward_workspace_size(n_q, H, top_k) bytes.  d_kv takes fp32 atomic
+ * adds, so its low-order bits depend on the order of the rows' contributions.
+ * ------------------------------------------------------------------------------------- */
+size_t dsa_sparse_mqa_backward_workspace_size(int32_t n_q, int32_t H, int32_t top_k);
+
+dsa_status dsa_sparse_mqa_backward(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
+                                   const int32_t* idx, const int32_t* q_pos, const uint16_t* out,
+                                   const float* lse, const uint16_t* d_out, int32_t n_q,
+                                   int32_t H, int32_t D_k, int32_t D_v, int32_t top_k,
+                                   float scale, float* d_q, float* d_kv, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Cache write: append new tokens to the paged caches the decode calls read.  Defines the step
  * just before the paged indexer and attention: the indexer keeps its keys in FP8 (jdon.com
  * "DeepSeek-V3.2-Exp" article, paragraph on the lightning indexer) in 64-token pages

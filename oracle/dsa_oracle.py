@@ -322,6 +322,44 @@ def indexer_kl(inp: dict, idx, rows=None):
     return loss, target, grad
 
 
+def sparse_mqa_backward(inp: dict, idx, d_out):
+    """Gradients of sum(d_out * o) with respect to q and the KV rows, o the sparse MQA output of
+    every query row over its index list (the selection itself is not differentiated).  In the
+    sparse training stage the model's loss reaches the attention through the selected entries
+    only (jdon.com article, sparse-training paragraph).  Per row, over the listed rows K (V =
+    their first D_v dims):  P = softmax(scale q K^T),  o = P V,  dP = dO V^T,
+    dS = P (dP - rowsum(dO o)),  dq = scale dS K,  dK = scale dS^T q,  dV = P^T dO, the last
+    two added into the listed KV rows (a row listed several times collects each share).
+    Returns (dq [n, H, D_k], dkv [n_kv, D_k]).
+    """
+    q_pos = _np(inp["q_pos"]).astype(np.int64)
+    kv = decode_bf16(inp["kv"])
+    d_v, scale = int(inp["D_v"]), float(inp["scale"])
+    idx = np.asarray(idx)
+    n, H = q_pos.shape[0], inp["q"].shape[1]
+    dq = np.zeros((n, H, kv.shape[1]))
+    dkv = np.zeros_like(kv)
+    for i in range(n):
+        t = min(int(q_pos[i]), kv.shape[0] - 1)
+        sel = valid_selected(idx[i], t)
+        if sel.size == 0:
+            continue
+        q = decode_bf16(inp["q"][i])
+        K = kv[sel]
+        V = K[:, :d_v]
+        z = scale * (q @ K.T)
+        P = np.exp(z - z.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        o = P @ V
+        dO = decode_bf16(d_out[i])
+        dS = P * (dO @ V.T - (dO * o).sum(axis=1, keepdims=True))
+        dq[i] = scale * (dS @ K)
+        dK = scale * (dS.T @ q)
+        dK[:, :d_v] += P.T @ dO
+        np.add.at(dkv, sel, dK)
+    return dq, dkv
+
+
 def dense_prefill(inp: dict, rows=None):
     """Dense causal attention, the baseline DSA replaces: row t attends every position 0..t
     (t = q_pos, clamped to the KV rows; t < 0 attends nothing).  Returns (o [n,H,D_v],
@@ -504,6 +542,7 @@ __all__ = [
     "E4M3FN", "decode_e4m3fn", "decode_bf16", "indexer_scores", "topk_select", "sparse_mqa",
     "valid_selected", "prefill_indexer_topk", "prefill", "paged_gather", "paged_rows", "decode",
     "batched_prefill", "dense_prefill", "dense_decode", "kl_from_scores", "indexer_kl",
+    "sparse_mqa_backward",
     "quantize_e4m3fn", "cache_append",
     "row_work",
     "causal_pairs", "selected_pairs",

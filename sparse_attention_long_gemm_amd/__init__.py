@@ -53,6 +53,9 @@ SIGNATURES = {
                                             _P, _P, _Z, _P]),
     "dsa_indexer_kl": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _I,
                                       _I, _P, _P, _P, _P]),
+    "dsa_sparse_mqa_backward_workspace_size": (_Z, [_I, _I, _I]),
+    "dsa_sparse_mqa_backward": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                               _F, _P, _P, _P, _Z, _P]),
     "dsa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dsa_sparse_mqa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                      _I, _I, _I, _F, _I, _P, _P, _P]),
@@ -423,6 +426,42 @@ def indexer_kl(q, kv, idx, q_pos, lse, scale: float, q_idx, w, k_idx, want_grad:
     return loss, target, grad
 
 
+def sparse_mqa_backward(q, kv, idx, q_pos, out, lse, d_out, scale: float, d_kv=None,
+                        workspace=None):
+    """Gradients of sum(d_out * out) for dsa_sparse_mqa_prefill's attention
+    (dsa_sparse_mqa_backward): returns (d_q fp32 [n_q, H, D_k], d_kv fp32 [n_kv, D_k]).  A given
+    d_kv is accumulated into (a new one starts at zero)."""
+    lib = load_library()
+    _need(q, "q", _BF16, 3)
+    dev = q.device
+    n_q, H, D_k = q.shape
+    _need(kv, "kv", _BF16, 2, dev)
+    n_kv = kv.shape[0]
+    _need(idx, "idx", _I32, 2, dev)
+    top_k = idx.shape[1]
+    _need(idx, "idx", _I32, 2, dev, shape=(n_q, top_k))
+    _need(q_pos, "q_pos", _I32, 1, dev, shape=(n_q,))
+    _need(out, "out", _BF16, 3, dev)
+    d_v = out.shape[2]
+    _need(out, "out", _BF16, 3, dev, shape=(n_q, H, d_v))
+    _need(lse, "lse", _F32, 2, dev, shape=(n_q, H))
+    _need(d_out, "d_out", _BF16, 3, dev, shape=(n_q, H, d_v))
+    if kv.shape[1] != D_k:
+        raise ValueError("kv rows do not match q")
+    d_q = torch.empty((n_q, H, D_k), dtype=torch.float32, device=dev)
+    if d_kv is None:
+        d_kv = torch.zeros((n_kv, D_k), dtype=torch.float32, device=dev)
+    _need(d_kv, "d_kv", _F32, 2, dev, shape=(n_kv, D_k))
+    nbytes = int(lib.dsa_sparse_mqa_backward_workspace_size(n_q, H, top_k))
+    ws, nb = _workspace(nbytes, dev, workspace)
+    _check(lib.dsa_sparse_mqa_backward(_ptr(q), _ptr(kv), n_kv, _ptr(idx), _ptr(q_pos), _ptr(out),
+                                       _ptr(lse), _ptr(d_out), n_q, H, D_k, d_v, top_k,
+                                       float(scale), _ptr(d_q), _ptr(d_kv), _ptr(ws), nb,
+                                       _stream(dev)),
+           "dsa_sparse_mqa_backward")
+    return d_q, d_kv
+
+
 def cache_append(page_table, pos, k_cache=None, kv_cache=None, k_new=None, kv_new=None,
                  seq=None):
     """Append new tokens to the paged caches (dsa_cache_append): k_new [T, d_I] bf16 is
@@ -505,7 +544,7 @@ def sparse_mqa_decode_noalloc(q, kv_cache, page_table, ctx_lens, idx, d_v: int, 
 __all__ = ["load_library", "DSAError", "indexer_topk", "indexer_topk_paged",
            "sparse_mqa_prefill", "sparse_mqa_decode", "sparse_mqa_decode_noalloc", "cache_append",
            "indexer_topk_batched", "sparse_mqa_batched", "dense_mqa_prefill",
-           "dense_mqa_decode", "dense_mqa_workspace_size", "indexer_kl",
+           "dense_mqa_decode", "dense_mqa_workspace_size", "indexer_kl", "sparse_mqa_backward",
            "indexer_topk_workspace_size",
            "indexer_topk_paged_workspace_size", "sparse_mqa_decode_workspace_size",
            "SIGNATURES", "LIB_PATH"]

@@ -254,6 +254,37 @@ dsa_status dsa_indexer_kl(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
                                          target, loss, grad, stream));
 }
 
+size_t dsa_sparse_mqa_backward_workspace_size(int32_t n_q, int32_t H, int32_t top_k) {
+  if (n_q < 0 || H < 1 || top_k < 1) return 0;
+  return 2 * (size_t)n_q * H * top_k * sizeof(uint16_t);
+}
+
+dsa_status dsa_sparse_mqa_backward(const uint16_t* q, const uint16_t* kv, int32_t n_kv,
+                                   const int32_t* idx, const int32_t* q_pos, const uint16_t* out,
+                                   const float* lse, const uint16_t* d_out, int32_t n_q,
+                                   int32_t H, int32_t D_k, int32_t D_v, int32_t top_k,
+                                   float scale, float* d_q, float* d_kv, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  if (n_q < 0 || n_kv < 1 || !isfinite(scale)) return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > kMaxH || !dsa::mqa_shape_supported(D_k, D_v) || top_k < 1 ||
+      top_k > kMaxTopK)
+    return DSA_ERR_UNSUPPORTED_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (n_q > 0x7fffffff / 2 || !q || !kv || !idx || !q_pos || !out || !lse || !d_out || !d_q ||
+      !d_kv)
+    return DSA_ERR_INVALID_ARG;
+  const size_t half = (size_t)n_q * H * top_k;
+  if (!workspace || workspace_bytes < dsa_sparse_mqa_backward_workspace_size(n_q, H, top_k))
+    return DSA_ERR_WORKSPACE_TOO_SMALL;
+  dsa::MqaArgs a{};
+  a.q = q; a.kv = kv; a.idx = idx; a.qpos_or_ctx = q_pos; a.n_kv = n_kv; a.n_q = n_q; a.H = H;
+  a.D_k = D_k; a.D_v = D_v; a.top_k = top_k; a.scale = scale; a.n_split = 1;
+  a.rows_per_split = top_k;
+  uint16_t* p_ws = reinterpret_cast<uint16_t*>(workspace);
+  return from_hip(dsa::launch_mqa_backward(a, lse, out, d_out, p_ws, p_ws + half, d_q, d_kv,
+                                           stream));
+}
+
 dsa_status dsa_cache_append(const uint16_t* k_new, const uint16_t* kv_new, const int32_t* seq,
                             const int32_t* pos, const int32_t* page_table, int32_t T,
                             int32_t max_pages, int32_t n_pages, int32_t page_size, int32_t d_I,

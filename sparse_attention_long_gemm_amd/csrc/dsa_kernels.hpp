@@ -65,6 +65,11 @@ int dense_rows_per_split();
 // (contiguous rows, n_split = 1), from the forward's natural-log lse.
 hipError_t launch_mqa_probs(const MqaArgs& a, const float* lse_in, float* probs,
                             hipStream_t stream);
+// Sparse MQA backward (contiguous rows): P / dS to the workspace, dQ (fp32, written), dKV
+// (fp32, accumulated with atomics).
+hipError_t launch_mqa_backward(const MqaArgs& a, const float* lse_in, const uint16_t* o_fwd,
+                               const uint16_t* d_out, uint16_t* p_ws, uint16_t* ds_ws,
+                               float* dq, float* dkv, hipStream_t stream);
 
 // Bytes of the per-device static scratch array of the allocation-free decode entry point.
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;

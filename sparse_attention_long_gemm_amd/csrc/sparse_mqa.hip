@@ -190,6 +190,24 @@ __host__ __device__ constexpr int vm_wait_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// What a launch of the kernel computes.
+enum MqaMode : int {
+  MODE_FWD = 0,     // attention output (and lse)
+  MODE_PROBS = 1,   // head-averaged probabilities of the listed entries (indexer KL target)
+  MODE_BWDP = 2,    // backward, first pass: P and dS = P (dP - rowsum(dO o O)) per entry
+  MODE_DQ = 3,      // backward, second pass: dQ = scale dS K over the listed rows
+};
+
+// Mode-specific operands.
+struct MqaAux {
+  float* probs;            // PROBS: out [n, top_k]
+  const uint16_t* d_out;   // BWDP: dO [n, H, DV] bf16
+  const uint16_t* o_fwd;   // BWDP: the forward's output O [n, H, DV] bf16
+  uint16_t* p_ws;          // BWDP: out P [n, H, top_k] bf16
+  uint16_t* ds_ws;         // BWDP: out dS [n, H, top_k] bf16; DQ: in
+  float* dq;               // DQ: out [n, H, DK] fp32
+};
+
 // PAGED rows read their KV rows through a page table: in decode (n_seq == 0) row qi is
 // sequence qi with t = ctx[qi] - 1; in a batched prefill (n_seq > 0) row qi is sequence
 // q_seq[qi] (0 when q_seq is NULL; a sequence outside [0, n_seq) attends nothing) with
@@ -197,11 +215,16 @@ __host__ __device__ constexpr int vm_wait_imm(int n) {
 // DENSE: the rows attended are all positions 0..t (dense causal attention, the baseline the
 // selection is measured against); split sp takes positions [sp * rows_per_split, ...), and
 // `idx` is not read.
-// PROBS: no attention output; instead, for every entry of the row's index list, the main
+// MODE_PROBS: no attention output; instead, for every entry of the row's index list, the main
 // attention's probability summed over the heads and divided by H, from the logits recomputed
 // here and the forward's log-sum-exp `lse` (read, natural log): probs[qi, e] =
 // (1/H) sum_h exp(scale q_h . kv_s - lse_h), 0 for an entry that is not attended.
-template <int DK, int DV, bool PAGED, bool DENSE, bool PROBS = false>
+// MODE_BWDP: with the forward's lse (read) and output O, and the output gradient dO: per head
+// and entry P = exp(scale q . kv - lse), dP = dO . v, dS = P (dP - sum_d dO O); P and dS go to
+// the workspace in bf16 (0 for entries not attended).
+// MODE_DQ: dQ[h] = scale sum_e dS[h, e] kv_e (all DK dims; instantiated with DV = DK), dS read
+// from the workspace; fp32 output.
+template <int DK, int DV, bool PAGED, bool DENSE, int MODE = MODE_FWD>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ qpos_or_ctx,
@@ -209,9 +232,14 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     int max_pages, int n_pages, int page_size, int n_kv,
     int H, int top_k, float scale_log2, int n_split, int rows_per_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_ml, float* __restrict__ probs) {
+    float* __restrict__ part_ml, MqaAux aux) {
   static_assert(DK % 32 == 0 && DV % 16 == 0 && DV <= DK, "shape");
-  static_assert(!(PROBS && (PAGED || DENSE)), "probabilities: contiguous sparse rows only");
+  constexpr bool PROBS = MODE == MODE_PROBS;
+  constexpr bool BWDP = MODE == MODE_BWDP;
+  constexpr bool DQM = MODE == MODE_DQ;
+  static_assert(MODE == MODE_FWD || (!PAGED && !DENSE), "contiguous sparse rows only");
+  static_assert(!DQM || DV == DK, "dQ mode covers every dimension");
+  float* __restrict__ probs = aux.probs;
   using Sh = MqaShared;
   constexpr int NKS = DK / 32;           // k-steps of the S^T product
   constexpr int NDB = DV / 16;           // 16-dim blocks of the output
@@ -257,7 +285,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   // ---- queries: B operand of k-step ks = dims 32ks + 8g .. +8 of head `head` (issued first,
   // so that their latency overlaps the index and page-table reads below) ----
   v8bf qf[NKS];
-  {
+  if constexpr (!DQM) {
     const uint16_t* qrow = q + ((size_t)qi * H + (head_ok ? head : 0)) * DK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -265,6 +293,32 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       if (head_ok) x = ld16(qrow + 32 * ks + 8 * g);
       qf[ks] = as_v8bf(x);
     }
+  }
+
+  // ---- BWDP: the output gradient of this lane's head, as the B operand of dP^T = V dO^T
+  // (the queries' layout over the first DV dims), and D = sum_d dO O of the head ----
+  constexpr int NVS = DV / 32;
+  v8bf dof[BWDP ? NVS : 1];
+  float dlt = 0.f;
+  if constexpr (BWDP) {
+    static_assert(DV % 32 == 0, "dP k-steps");
+    const size_t ro = ((size_t)qi * H + (head_ok ? head : 0)) * DV;
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NVS; ++ks) {
+      v4i x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+      if (head_ok) {
+        x = ld16(aux.d_out + ro + 32 * ks + 8 * g);
+        y = ld16(aux.o_fwd + ro + 32 * ks + 8 * g);
+      }
+      dof[ks] = as_v8bf(x);
+      const v8bf yo = as_v8bf(y);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part = fmaf((float)dof[ks][j], (float)yo[j], part);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    dlt = part;
   }
 
   // ---- physical row of every selected entry (-1: skipped); all index reads of a thread are
@@ -349,7 +403,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   // PROBS: this lane's head's log-sum-exp in log2 units; the chunk sums are written out one
   // step later by wave 0 (the barrier at the end of each step separates the two buffers' uses)
   float lse2 = 0.f;
-  if constexpr (PROBS) lse2 = head_ok ? lse[(size_t)qi * H + head] * 1.4426950408889634f : 0.f;
+  if constexpr (PROBS || BWDP)
+    lse2 = head_ok ? lse[(size_t)qi * H + head] * 1.4426950408889634f : 0.f;
   const float inv_h = 1.f / (float)H;
   auto flush_probs = [&](int cc) {
     if (wave == 0 && lane < CH) {
@@ -368,6 +423,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 
     // ---- S^T = K Q^T: 32 keys (two blocks of 16) x this wave's 16 heads ----
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    v4f dp0 = {0.f, 0.f, 0.f, 0.f}, dp1 = {0.f, 0.f, 0.f, 0.f};   // BWDP: dP^T
     const lds_u8* b0 = tile + qk_off0;
     const lds_u8* b1 = tile + qk_off1;
     v4i ka[QPD], kb[QPD];
@@ -375,15 +431,25 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       ka[k % QPD] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(b0 + 64 * k);
       kb[k % QPD] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(b1 + 64 * k);
     };
+    if constexpr (!DQM) {
 #pragma unroll
-    for (int ks = 0; ks < QPD && ks < NKS; ++ks) fetch(ks);
+      for (int ks = 0; ks < QPD && ks < NKS; ++ks) fetch(ks);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const v4i a0 = ka[ks % QPD], a1 = kb[ks % QPD];
-      const v8bf bq = qf[ks];
-      if (ks + QPD < NKS) fetch(ks + QPD);
-      s0 = mfma16_bf16(as_v8bf(a0), bq, s0);
-      s1 = mfma16_bf16(as_v8bf(a1), bq, s1);
+      if constexpr (!DQM) {
+        const v4i a0 = ka[ks % QPD], a1 = kb[ks % QPD];
+        const v8bf bq = qf[ks];
+        if (ks + QPD < NKS) fetch(ks + QPD);
+        s0 = mfma16_bf16(as_v8bf(a0), bq, s0);
+        s1 = mfma16_bf16(as_v8bf(a1), bq, s1);
+        if constexpr (BWDP) {
+          if (ks < NVS) {   // the same key rows' first DV dims are V
+            dp0 = mfma16_bf16(as_v8bf(a0), dof[ks < NVS ? ks : 0], dp0);
+            dp1 = mfma16_bf16(as_v8bf(a1), dof[ks < NVS ? ks : 0], dp1);
+          }
+        }
+      }
       const int j0 = first_load_at<NKS, GJ>(ks), j1 = first_load_at<NKS, GJ>(ks + 1);
       if (j0 < j1 && more) gather_chunk<DK>(gtile, kv, row_nx, wave, lane, j0, j1, slot_off);
       __builtin_amdgcn_sched_barrier(0);
@@ -408,11 +474,42 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
         for (int i = 0; i < 8; ++i)
           atomicAdd(&psh[c & 1][(i < 4 ? 0 : 16) + 4 * g + (i & 3)], pv[i]);
       }
+    } else if constexpr (BWDP) {
+      // P and dS of this lane's 8 entries for its head, to the workspace (bf16, 0 for entries
+      // that are not attended)
+      const u32 vmp = vmask >> (4 * g);
+      const size_t wb = ((size_t)qi * H + head) * top_k + r0 + c * CH;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = i < 4 ? s0[i & 3] : s1[i & 3];
+        const float dpv = i < 4 ? dp0[i & 3] : dp1[i & 3];
+        const bool ok = head_ok && ((vmp >> ((i < 4 ? 0 : 16) + (i & 3))) & 1u);
+        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(x, scale_log2, -lse2)) : 0.f;
+        const float dsv = pv * (dpv - dlt);
+        const int e = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
+        if (head_ok && c * CH + e < nrows) {
+          aux.p_ws[wb + e] = f32_to_bf16(pv);
+          aux.ds_ws[wb + e] = f32_to_bf16(dsv);
+        }
+      }
+    } else {
+    v8bf pb;
+    if constexpr (DQM) {
+      // dS of this lane's 8 entries (the value product's k slots follow them), from the
+      // workspace; 0 past the row's entries
+      const size_t wb = ((size_t)qi * H + (head_ok ? head : 0)) * top_k + r0 + c * CH;
+      uint16_t bits[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
+        bits[i] = 0;
+        if (head_ok && c * CH + e < nrows) bits[i] = aux.ds_ws[wb + e];
+      }
+      __builtin_memcpy(&pb, bits, 16);
     } else {
     // ---- online softmax: lane holds keys 4g + i (s0) and 16 + 4g + i (s1) of head h16 ----
     const u32 vml = vmask >> (4 * g);   // bit i: key 4g + i; bit 16 + i: key 16 + 4g + i
     float psum = 0.f;
-    v8bf pb;
     auto prob_pass = [&](float m_use, auto masked) {
       float mx = -__builtin_inff();
       psum = 0.f;
@@ -455,8 +552,9 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       }
     }
     l_run += psum;
+    }   // FWD softmax
 
-    // ---- O^T += V^T P^T over the 32 keys, 16 dims per block ----
+    // ---- O^T += V^T P^T over the 32 keys, 16 dims per block (DQ: dQ^T += K^T dS^T) ----
     const lds_u8* tr_base = tile + tr_off;
     constexpr int VPD = 4;
     v4s fa[VPD], fb[VPD];
@@ -476,7 +574,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       o[d] = mfma16_bf16(a, pb, o[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    }   // !PROBS
+    }   // FWD / DQ
     vm_a = vm_b;
     vm_b = (u32)wave_ballot(row_nx >= 0);
     row_nx = chunk_row(c + 3);
@@ -499,6 +597,17 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
 
   if constexpr (PROBS) {
     if (n_chunks > 0) flush_probs(n_chunks - 1);   // after the last step's barrier
+    return;
+  }
+  if constexpr (BWDP) return;
+  if constexpr (DQM) {
+    // dQ = scale * sum_e dS kv_e (scale_log2 = scale * log2 e)
+    if (!head_ok) return;
+    const float sc = scale_log2 * 0.69314718055994531f;
+    float* dqr = aux.dq + ((size_t)qi * H + head) * DK;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+      *reinterpret_cast<v4f*>(dqr + 16 * d + 4 * g) = o[d] * sc;
     return;
   }
 
@@ -649,12 +758,12 @@ hipError_t launch_dense_shape(const MqaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, true>), dim3(a.n_q, a.n_split),
                        dim3(NT), 0, stream, a.q, a.kv, nullptr, a.qpos_or_ctx, nullptr, nullptr,
                        0, 0, 0, 1, a.n_kv, a.H, 0, scale_log2, a.n_split, rps, a.out, a.lse,
-                       a.part_o, a.part_ml, nullptr);
+                       a.part_o, a.part_ml, MqaAux{});
   else
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true, true>), dim3(a.n_q, a.n_split),
                        dim3(NT), 0, stream, a.q, a.kv, nullptr, a.qpos_or_ctx, a.page_table,
                        nullptr, 0, a.max_pages, a.n_pages, a.page_size, 0, a.H, 0, scale_log2,
-                       a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml, nullptr);
+                       a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml, MqaAux{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   return launch_combine<DV>(a, stream);
@@ -667,14 +776,14 @@ hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, false>), dim3(a.n_q, 1), dim3(NT), 0, stream,
                        a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0, 0, 1, a.n_kv,
                        a.H, a.top_k, scale_log2, 1, a.top_k, a.out, a.lse, nullptr, nullptr,
-                       nullptr);
+                       MqaAux{});
     return hipGetLastError();
   }
   const int rps = a.rows_per_split;
   hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true, false>), dim3(a.n_q, a.n_split), dim3(NT), 0,
                      stream, a.q, a.kv, a.idx, a.qpos_or_ctx, a.page_table, a.q_seq, a.n_seq,
                      a.max_pages, a.n_pages, a.page_size, 0, a.H, a.top_k, scale_log2,
-                     a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml, nullptr);
+                     a.n_split, rps, a.out, a.lse, a.part_o, a.part_ml, MqaAux{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   return launch_combine<DV>(a, stream);
@@ -733,15 +842,129 @@ hipError_t launch_dense_mqa(const MqaArgs& a, hipStream_t stream) {
 
 int dense_rows_per_split() { return MAX_ROWS; }
 
+// Backward, third pass: dKV.  For every listed entry e of row t (KV row s):
+//   dKV[s, :] += scale sum_h dS[h, e] q[t, h, :] + sum_h P[h, e] dO[t, h, :DV] (0 past DV),
+// added with fp32 atomics (a row is listed by many queries).  One workgroup per query row;
+// the P and dS of 32 entries at a time are staged in LDS (read as broadcasts), each thread
+// owns the dims tid, tid + 256, ... of the 32 entries' gradients.
+constexpr int DKV_NT = 256;
+
+template <int DK, int DV>
+__global__ __launch_bounds__(DKV_NT) void mqa_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_out,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ q_pos, int n_kv, int H,
+    int top_k, float scale, const uint16_t* __restrict__ p_ws,
+    const uint16_t* __restrict__ ds_ws, float* __restrict__ d_kv) {
+  constexpr int NDJ = (DK + DKV_NT - 1) / DKV_NT;
+  __shared__ float sds[CH][128];
+  __shared__ float sp[CH][128];
+  __shared__ int srow[CH];
+  const int qi = blockIdx.x, tid = threadIdx.x;
+  int t = q_pos[qi];
+  if (t > n_kv - 1) t = n_kv - 1;
+  for (int c0 = 0; c0 < top_k; c0 += CH) {
+    const int ne = min(CH, top_k - c0);
+    if (tid < CH) {
+      const int sv = tid < ne ? idx[(size_t)qi * top_k + c0 + tid] : -1;
+      srow[tid] = (sv >= 0 && sv <= t) ? sv : -1;
+    }
+    for (int i = tid; i < H * CH; i += DKV_NT) {
+      const int h = i / CH, e = i - h * CH;
+      float dsv = 0.f, pv = 0.f;
+      if (e < ne) {
+        const size_t o = ((size_t)qi * H + h) * top_k + c0 + e;
+        dsv = bf16_to_f32(ds_ws[o]);
+        pv = bf16_to_f32(p_ws[o]);
+      }
+      sds[e][h] = dsv * scale;
+      sp[e][h] = pv;
+    }
+    __syncthreads();
+    float acc[CH][NDJ];
+#pragma unroll
+    for (int e = 0; e < CH; ++e)
+#pragma unroll
+      for (int j = 0; j < NDJ; ++j) acc[e][j] = 0.f;
+#pragma unroll 1
+    for (int h = 0; h < H; ++h) {
+      float qd[NDJ], od[NDJ];
+#pragma unroll
+      for (int j = 0; j < NDJ; ++j) {
+        const int d = tid + DKV_NT * j;
+        qd[j] = d < DK ? bf16_to_f32(q[((size_t)qi * H + h) * DK + d]) : 0.f;
+        od[j] = d < DV ? bf16_to_f32(d_out[((size_t)qi * H + h) * DV + d]) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const float a = sds[e][h], b = sp[e][h];
+#pragma unroll
+        for (int j = 0; j < NDJ; ++j) acc[e][j] = fmaf(a, qd[j], fmaf(b, od[j], acc[e][j]));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int sr = srow[e];
+      if (sr < 0) continue;
+#pragma unroll
+      for (int j = 0; j < NDJ; ++j) {
+        const int d = tid + DKV_NT * j;
+        if (d < DK) atomicAdd(&d_kv[(size_t)sr * DK + d], acc[e][j]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_backward_shape(const MqaArgs& a, const float* lse_in, const uint16_t* o_fwd,
+                                 const uint16_t* d_out, uint16_t* p_ws, uint16_t* ds_ws,
+                                 float* dq, float* dkv, hipStream_t stream) {
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  MqaAux aux{};
+  aux.d_out = d_out;
+  aux.o_fwd = o_fwd;
+  aux.p_ws = p_ws;
+  aux.ds_ws = ds_ws;
+  aux.dq = dq;
+  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, false, MODE_BWDP>), dim3(a.n_q, 1),
+                     dim3(NT), 0, stream, a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0,
+                     0, 1, a.n_kv, a.H, a.top_k, scale_log2, 1, a.top_k, nullptr,
+                     const_cast<float*>(lse_in), nullptr, nullptr, aux);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DK, false, false, MODE_DQ>), dim3(a.n_q, 1),
+                     dim3(NT), 0, stream, a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0,
+                     0, 1, a.n_kv, a.H, a.top_k, scale_log2, 1, a.top_k, nullptr, nullptr,
+                     nullptr, nullptr, aux);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((mqa_dkv_kernel<DK, DV>), dim3(a.n_q), dim3(DKV_NT), 0, stream, a.q, d_out,
+                     a.idx, a.qpos_or_ctx, a.n_kv, a.H, a.top_k, a.scale, p_ws, ds_ws, dkv);
+  return hipGetLastError();
+}
+
 template <int DK, int DV>
 hipError_t launch_probs_shape(const MqaArgs& a, const float* lse_in, float* probs,
                               hipStream_t stream) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, false, true>), dim3(a.n_q, 1), dim3(NT),
-                     0, stream, a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0, 0, 1,
-                     a.n_kv, a.H, a.top_k, scale_log2, 1, a.top_k, nullptr,
-                     const_cast<float*>(lse_in), nullptr, nullptr, probs);
+  MqaAux aux{};
+  aux.probs = probs;
+  hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, false, false, MODE_PROBS>), dim3(a.n_q, 1),
+                     dim3(NT), 0, stream, a.q, a.kv, a.idx, a.qpos_or_ctx, nullptr, nullptr, 0, 0,
+                     0, 1, a.n_kv, a.H, a.top_k, scale_log2, 1, a.top_k, nullptr,
+                     const_cast<float*>(lse_in), nullptr, nullptr, aux);
   return hipGetLastError();
+}
+
+hipError_t launch_mqa_backward(const MqaArgs& a, const float* lse_in, const uint16_t* o_fwd,
+                               const uint16_t* d_out, uint16_t* p_ws, uint16_t* ds_ws,
+                               float* dq, float* dkv, hipStream_t stream) {
+  if (a.D_k == 576 && a.D_v == 512)
+    return launch_backward_shape<576, 512>(a, lse_in, o_fwd, d_out, p_ws, ds_ws, dq, dkv, stream);
+  if (a.D_k == 64 && a.D_v == 64)
+    return launch_backward_shape<64, 64>(a, lse_in, o_fwd, d_out, p_ws, ds_ws, dq, dkv, stream);
+  if (a.D_k == 96 && a.D_v == 64)
+    return launch_backward_shape<96, 64>(a, lse_in, o_fwd, d_out, p_ws, ds_ws, dq, dkv, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_mqa_probs(const MqaArgs& a, const float* lse_in, float* probs,

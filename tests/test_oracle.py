@@ -458,6 +458,36 @@ def test_indexer_kl_target_is_the_head_mean_of_softmax():
     assert target[100, 3] == 0 and target[100, 4] == 0 and grad[100, 4] == 0
 
 
+# --------------------------------------------------------------------------- backward
+
+def test_sparse_backward_equals_torch_autograd():
+    """The analytic gradients equal torch autograd (fp64, CPU) of sum(d_out * o) through the
+    gathered rows, softmax and value product; rows with -1 and out-of-range entries, and a KV
+    row listed by many queries, included."""
+    wl = gi.Workload(name="bw", L=80, idx=gi.IndexerSpec(H_I=4, d_I=32, top_k=16),
+                     mqa=gi.MqaSpec(H=3, D_k=96, D_v=64, sigma=1.0, scale=96 ** -0.5), seed=21)
+    d = gi.prefill_inputs(wl)
+    idx = orc.prefill_indexer_topk(d)
+    idx[40, 2] = -1
+    idx[41, 0] = 79            # beyond t: not attended
+    g = torch.Generator().manual_seed(22)
+    d_out = torch.randn((80, 3, 64), generator=g).to(torch.bfloat16)
+    dq, dkv = orc.sparse_mqa_backward(d, idx, d_out)
+    q = d["q"].double().requires_grad_(True)
+    kv = d["kv"].double().requires_grad_(True)
+    total = 0.0
+    for t in range(80):
+        sel = torch.tensor([s for s in idx[t] if 0 <= s <= t], dtype=torch.long)
+        K = kv[sel]
+        z = (q[t] @ K.T) * 96 ** -0.5
+        o = torch.softmax(z, dim=1) @ K[:, :64]
+        total = total + (o * d_out[t].double()).sum()
+    total.backward()
+    assert np.allclose(dq, q.grad.numpy(), rtol=0, atol=1e-11)
+    assert np.allclose(dkv, kv.grad.numpy(), rtol=0, atol=1e-11)
+    assert np.abs(dkv).max() > 0.1 and np.abs(dq).max() > 0.1
+
+
 # --------------------------------------------------------------------------- batched prefill
 
 def _contiguous_of(d, b, rows):
