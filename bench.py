@@ -42,6 +42,9 @@ KERNEL_SOURCES = {
 PEAK_FP8 = 5.0e15      # dense FP8 MFMA, FLOP/s (MI355X published)
 PEAK_BF16 = 2.5e15     # dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12      # HBM3E, B/s
+# fp32 FMA on the vector units without packed math (256 CUs x 4 SIMDs x 16 lanes x 2 flop x
+# 2.4 GHz); the packed-math figure of 157.3 TFLOP/s does not apply: packed fp32 is not used
+PEAK_VALU_FP32 = 78.6e12
 
 
 def causal_pairs_range(q0, q1):
@@ -393,6 +396,47 @@ def extra_legs(pre: Prefill, dec: Decode, dev, reps: int):
         "indexer_frac": vl.flops_idx / t_i / PEAK_FP8, "mqa_frac": vl.flops_mqa / t_m / PEAK_BF16,
         "frac_of_roofline": (vl.flops_idx / PEAK_FP8 + vl.flops_mqa / PEAK_BF16) / (t_i + t_m)}
     del vl
+    torch.cuda.empty_cache()
+    # training-side rows on the last 4096-row block of the prefill (its indices are the last
+    # ones the block loop left in pre.idx; out and lse hold every row)
+    a, e = pre.blocks[-1]
+    d, m, ix = pre.inp, pre.wl.mqa, pre.wl.idx
+    n = e - a
+    idx_b = pre.idx[:n]
+    dsa = pre.dsa
+
+    def kl():
+        dsa.indexer_kl(d["q"][a:e], d["kv"][:e], idx_b, d["q_pos"][a:e], pre.lse[a:e], m.scale,
+                       d["q_idx"][a:e], d["w"][a:e], d["k_idx"][:e])
+    kl()
+    t = _time(kl, reps) * 1e-3
+    pairs = selected_pairs_range(a, e, pre.top_k)
+    f_bf16, f_fp8 = 2.0 * m.H * m.D_k * pairs, 2.0 * ix.H_I * ix.d_I * pairs
+    out["indexer_kl"] = {
+        "workload": f"rows {a}..{e - 1} of the L=131072 prefill, their 2048 selected keys",
+        "ms": t * 1e3, "frac_of_roofline": (f_bf16 / PEAK_BF16 + f_fp8 / PEAK_FP8) / t,
+        "algorithmic": "per selected pair 2*H*D_k bf16 (logits) + 2*H_I*d_I FP8 (rescoring)"}
+    g = torch.Generator(device=dev).manual_seed(3)
+    d_out = torch.randn((n, m.H, m.D_v), generator=g, device=dev).to(torch.bfloat16)
+    d_kv = torch.zeros((e, m.D_k), dtype=torch.float32, device=dev)
+    ws_b = torch.empty(int(dsa.load_library().dsa_sparse_mqa_backward_workspace_size(
+        n, m.H, pre.top_k)), dtype=torch.uint8, device=dev)
+
+    def bwd():
+        dsa.sparse_mqa_backward(d["q"][a:e], d["kv"][:e], idx_b, d["q_pos"][a:e], pre.out[a:e],
+                                pre.lse[a:e], d_out, m.scale, d_kv=d_kv, workspace=ws_b)
+    bwd()
+    t = _time(bwd, reps) * 1e-3
+    f_mfma = 2.0 * m.H * (2 * m.D_k + m.D_v) * pairs      # logits, dP, dQ
+    f_valu = 2.0 * m.H * (m.D_k + m.D_v) * pairs          # dKV scatter
+    out["sparse_backward"] = {
+        "workload": f"rows {a}..{e - 1} of the L=131072 prefill (dQ, dKV)",
+        "ms": t * 1e3,
+        "frac_of_roofline": (f_mfma / PEAK_BF16 + f_valu / PEAK_VALU_FP32) / t,
+        "algorithmic": "per selected pair 2*H*(2*D_k+D_v) bf16 MFMA flop (logits, dP, dQ) + "
+                       "2*H*(D_k+D_v) fp32 VALU flop (dKV), against 2.5 PFLOP/s and "
+                       "78.6 TFLOP/s (fp32 FMA without packed math)"}
+    del d_out, d_kv, ws_b
     torch.cuda.empty_cache()
     dec.setup_append()
     dec.run_append()
