@@ -64,7 +64,10 @@ int dsa_abi_version(void);
 const char* dsa_status_string(int status);
 
 /* ---------------------------------------------------------------------------------------
- * Prefill indexer + top-k, one contiguous sequence.
+ * Prefill indexer + top-k, one contiguous sequence.  Defines steps 1-2 above: the lightning
+ * indexer's ReLU-activated, head-weighted FP8 score and the top_k selection (jdon.com
+ * "DeepSeek-V3.2-Exp" article, paragraphs on the lightning indexer and on fine-grained token
+ * selection; mundobytes.com page, section "Introduction of DeepSeek Sparse Attention (DSA)").
  *
  * q_idx   [n_q, H_I, d_I]  FP8   indexer queries of the n_q query rows
  * w       [n_q, H_I]       fp32  per-row head weights (any finite values, any sign)
@@ -94,6 +97,10 @@ dsa_status dsa_indexer_topk(const uint8_t* q_idx, const float* w, const uint8_t*
 
 /* ---------------------------------------------------------------------------------------
  * Decode indexer + top-k over a paged key cache: one new query per sequence at t = ctx-1.
+ * Steps 1-2 for one query per sequence over the cached keys, read through the page table of
+ * the serving recipe (mundobytes.com page, sections "Quick guide to running locally" and
+ * "Open kernels and ecosystem support": paged indexer logits; jdon.com article, paragraph on
+ * inference cost: decode revisits only the selected tokens).
  *
  * q_idx      [B, H_I, d_I]               FP8
  * w          [B, H_I]                    fp32
@@ -179,7 +186,9 @@ dsa_status dsa_sparse_mqa_batched(const uint16_t* q, const uint16_t* kv_cache,
                                   float scale, uint16_t* out, float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
- * Sparse MQA prefill over the selected rows of one contiguous sequence.
+ * Sparse MQA prefill over the selected rows of one contiguous sequence.  Step 3: attention
+ * in MQA mode over the selected shared latent rows only (openi.cn "DeepSeek-V3.2" page, item
+ * on MLA run in MQA mode; jdon.com article, paragraph on fine-grained token selection).
  *
  * q      [n_q, H, D_k]     bf16  queries
  * kv     [n_kv, D_k]       bf16  shared latent KV rows; K = whole row, V = first D_v dims
@@ -195,7 +204,9 @@ dsa_status dsa_sparse_mqa_prefill(const uint16_t* q, const uint16_t* kv, int32_t
                                   float scale, uint16_t* out, float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
- * Sparse MQA decode over a paged KV cache: one query per sequence, t = ctx-1.
+ * Sparse MQA decode over a paged KV cache: one query per sequence, t = ctx-1.  Step 3 for
+ * the decode query through the page table (openi.cn page, MLA/MQA item; mundobytes.com page,
+ * "Quick guide to running locally" for the 64-token pages).
  *
  * q        [B, H, D_k]                bf16
  * kv_cache [n_pages, page_size, D_k]  bf16  same paging as dsa_indexer_topk_paged
