@@ -269,6 +269,19 @@ def recorded_traffic(kernel: str):
     return rec["bytes_per_launch"]
 
 
+def recorded_decode_traffic():
+    """Per-kernel HBM bytes of one decode step and each kernel's L2 hit rate, from the same
+    counter runs (only while the sources match); {} otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            recs = json.load(fh)["decode_kernels"]
+    except (OSError, KeyError, ValueError):
+        return {}
+    dig = source_digest("decode_step")
+    return {k: {"bytes": v["bytes_per_launch"], "l2_hit_rate": v["l2_hit_rate"]}
+            for k, v in recs.items() if v.get("source_sha256") == dig}
+
+
 def copy_calibration(dev, nbytes=1 << 30, reps=3):
     """A plain elementwise copy of known size (fp32 negation: reads nbytes, writes nbytes) for
     scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -666,7 +679,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": dec_bytes / t_dec / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": dec_bytes / t_dec / PEAK_HBM,
                      "traffic": recorded_traffic("decode_step"),
-                     "algorithmic_bytes_per_step": dec_bytes},
+                     "algorithmic_bytes_per_step": dec_bytes,
+                     "traffic_per_kernel": recorded_decode_traffic()},
     }
     res = {
         "metric": "DSA prefill tokens/s at 128K (decode us/token alongside), % of MFMA/HBM roofline",
