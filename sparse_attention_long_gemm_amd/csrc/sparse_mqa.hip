@@ -203,8 +203,8 @@ struct MqaAux {
   float* probs;            // PROBS: out [n, top_k]
   const uint16_t* d_out;   // BWDP: dO [n, H, DV] bf16
   const uint16_t* o_fwd;   // BWDP: the forward's output O [n, H, DV] bf16
-  uint16_t* p_ws;          // BWDP: out P [n, H, top_k] bf16
-  uint16_t* ds_ws;         // BWDP: out dS [n, H, top_k] bf16; DQ: in
+  uint16_t* p_ws;          // BWDP: out P [n, top_k, H] bf16
+  uint16_t* ds_ws;         // BWDP: out scale * dS [n, top_k, H] bf16; DQ: in
   float* dq;               // DQ: out [n, H, DK] fp32
 };
 
@@ -220,9 +220,9 @@ struct MqaAux {
 // here and the forward's log-sum-exp `lse` (read, natural log): probs[qi, e] =
 // (1/H) sum_h exp(scale q_h . kv_s - lse_h), 0 for an entry that is not attended.
 // MODE_BWDP: with the forward's lse (read) and output O, and the output gradient dO: per head
-// and entry P = exp(scale q . kv - lse), dP = dO . v, dS = P (dP - sum_d dO O); P and dS go to
-// the workspace in bf16 (0 for entries not attended).
-// MODE_DQ: dQ[h] = scale sum_e dS[h, e] kv_e (all DK dims; instantiated with DV = DK), dS read
+// and entry P = exp(scale q . kv - lse), dP = dO . v, dS = P (dP - sum_d dO O); P and scale dS
+// go to the workspace in bf16, entry-major ([row][entry][head]; 0 for entries not attended).
+// MODE_DQ: dQ[h] = sum_e (scale dS)[h, e] kv_e (all DK dims; instantiated with DV = DK), read
 // from the workspace; fp32 output.
 template <int DK, int DV, bool PAGED, bool DENSE, int MODE = MODE_FWD>
 __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
@@ -478,18 +478,19 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       // P and dS of this lane's 8 entries for its head, to the workspace (bf16, 0 for entries
       // that are not attended)
       const u32 vmp = vmask >> (4 * g);
-      const size_t wb = ((size_t)qi * H + head) * top_k + r0 + c * CH;
+      const float sc = scale_log2 * 0.69314718055994531f;   // the softmax scale
+      const size_t wb = ((size_t)qi * top_k + r0 + c * CH) * H + head;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float x = i < 4 ? s0[i & 3] : s1[i & 3];
         const float dpv = i < 4 ? dp0[i & 3] : dp1[i & 3];
         const bool ok = head_ok && ((vmp >> ((i < 4 ? 0 : 16) + (i & 3))) & 1u);
         const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(x, scale_log2, -lse2)) : 0.f;
-        const float dsv = pv * (dpv - dlt);
+        const float dsv = pv * (dpv - dlt) * sc;
         const int e = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
         if (head_ok && c * CH + e < nrows) {
-          aux.p_ws[wb + e] = f32_to_bf16(pv);
-          aux.ds_ws[wb + e] = f32_to_bf16(dsv);
+          aux.p_ws[wb + (size_t)e * H] = f32_to_bf16(pv);
+          aux.ds_ws[wb + (size_t)e * H] = f32_to_bf16(dsv);
         }
       }
     } else {
@@ -497,13 +498,13 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
     if constexpr (DQM) {
       // dS of this lane's 8 entries (the value product's k slots follow them), from the
       // workspace; 0 past the row's entries
-      const size_t wb = ((size_t)qi * H + (head_ok ? head : 0)) * top_k + r0 + c * CH;
+      const size_t wb = ((size_t)qi * top_k + r0 + c * CH) * H + (head_ok ? head : 0);
       uint16_t bits[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
         bits[i] = 0;
-        if (head_ok && c * CH + e < nrows) bits[i] = aux.ds_ws[wb + e];
+        if (head_ok && c * CH + e < nrows) bits[i] = aux.ds_ws[wb + (size_t)e * H];
       }
       __builtin_memcpy(&pb, bits, 16);
     } else {
@@ -601,13 +602,11 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   }
   if constexpr (BWDP) return;
   if constexpr (DQM) {
-    // dQ = scale * sum_e dS kv_e (scale_log2 = scale * log2 e)
+    // dQ = sum_e (scale dS) kv_e (the workspace holds dS already scaled)
     if (!head_ok) return;
-    const float sc = scale_log2 * 0.69314718055994531f;
     float* dqr = aux.dq + ((size_t)qi * H + head) * DK;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
-      *reinterpret_cast<v4f*>(dqr + 16 * d + 4 * g) = o[d] * sc;
+    for (int d = 0; d < NDB; ++d) *reinterpret_cast<v4f*>(dqr + 16 * d + 4 * g) = o[d];
     return;
   }
 
@@ -843,75 +842,122 @@ hipError_t launch_dense_mqa(const MqaArgs& a, hipStream_t stream) {
 int dense_rows_per_split() { return MAX_ROWS; }
 
 // Backward, third pass: dKV.  For every listed entry e of row t (KV row s):
-//   dKV[s, :] += scale sum_h dS[h, e] q[t, h, :] + sum_h P[h, e] dO[t, h, :DV] (0 past DV),
-// added with fp32 atomics (a row is listed by many queries).  One workgroup per query row;
-// the P and dS of 32 entries at a time are staged in LDS (read as broadcasts), each thread
-// owns the dims tid, tid + 256, ... of the 32 entries' gradients.
-constexpr int DKV_NT = 256;
+//   dKV[s, :] += sum_h (scale dS)[e, h] q[t, h, :] + sum_h P[e, h] dO[t, h, :DV] (0 past DV),
+// i.e. per chunk of 32 entries the product C[entries x dims] = [scale dS | P] [q ; dO] with the
+// 2H heads as the contraction, on bf16 MFMAs (16x16x32), added into fp32 dKV with atomics (a
+// KV row is listed by many queries).  One workgroup (12 waves) per query row; wave w owns the
+// output dims [16 BPW w, 16 BPW (w + 1)).  The B operands (q and dO over the wave's dims, 8
+// heads per lane group) are gathered once per row and stay in registers; the A operands (8
+// consecutive heads of one entry) are 16-byte loads from the entry-major workspace.  Each
+// atomic instruction covers 16 consecutive dims of 4 KV rows.  The dims are split over
+// gridDim.y workgroups per row (DKV_BPW blocks per wave keep the operands in registers).
+constexpr int DKV_WAVES = 8;
+constexpr int DKV_NT = DKV_WAVES * kWave;
+constexpr int DKV_BPW = 3;                              // 16-dim blocks per wave
+constexpr int DKV_BLOCKS = DKV_WAVES * DKV_BPW;         // 16-dim blocks per workgroup
 
 template <int DK, int DV>
 __global__ __launch_bounds__(DKV_NT) void mqa_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_out,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ q_pos, int n_kv, int H,
-    int top_k, float scale, const uint16_t* __restrict__ p_ws,
-    const uint16_t* __restrict__ ds_ws, float* __restrict__ d_kv) {
-  constexpr int NDJ = (DK + DKV_NT - 1) / DKV_NT;
-  __shared__ float sds[CH][128];
-  __shared__ float sp[CH][128];
-  __shared__ int srow[CH];
-  const int qi = blockIdx.x, tid = threadIdx.x;
+    int top_k, const uint16_t* __restrict__ p_ws, const uint16_t* __restrict__ ds_ws,
+    float* __restrict__ d_kv) {
+  constexpr int NBLK = DK / 16;                                // 16-dim output blocks
+  constexpr int BPW = DKV_BPW;
+  constexpr int KS = 128 / 32;                                 // k-steps per part (H <= 128)
+  const int qi = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int g = lane >> 4, n16 = lane & 15;
   int t = q_pos[qi];
   if (t > n_kv - 1) t = n_kv - 1;
+  const int blk0 = blockIdx.y * DKV_BLOCKS + wave * BPW;
+  if (blk0 >= NBLK) return;                                    // wave-uniform
+  const int nks = (H + 31) / 32;                               // k-steps actually used
+
+  // ---- B operands: q[h, d] and dO[h, d] for d = 16 blk + n16, h = 32 ks + 8 g + j ----
+  v8bf bq[BPW][KS], bo[BPW][KS];
+#pragma unroll
+  for (int b = 0; b < BPW; ++b) {
+    const int d = 16 * (blk0 + b) + n16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint16_t vq[8], vo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int h = 32 * ks + 8 * g + j;
+        const bool okh = ks < nks && h < H && blk0 + b < NBLK;
+        vq[j] = okh ? q[((size_t)qi * H + h) * DK + d] : (uint16_t)0;
+        vo[j] = (okh && d < DV) ? d_out[((size_t)qi * H + h) * DV + d] : (uint16_t)0;
+      }
+      __builtin_memcpy(&bq[b][ks], vq, 16);
+      __builtin_memcpy(&bo[b][ks], vo, 16);
+      __builtin_amdgcn_sched_barrier(0);   // 16 gathers in flight at a time, not all 128
+    }
+  }
+  const bool heads8 = (H & 7) == 0;   // 8-head groups never straddle the row's end
+
   for (int c0 = 0; c0 < top_k; c0 += CH) {
-    const int ne = min(CH, top_k - c0);
-    if (tid < CH) {
-      const int sv = tid < ne ? idx[(size_t)qi * top_k + c0 + tid] : -1;
-      srow[tid] = (sv >= 0 && sv <= t) ? sv : -1;
-    }
-    for (int i = tid; i < H * CH; i += DKV_NT) {
-      const int h = i / CH, e = i - h * CH;
-      float dsv = 0.f, pv = 0.f;
-      if (e < ne) {
-        const size_t o = ((size_t)qi * H + h) * top_k + c0 + e;
-        dsv = bf16_to_f32(ds_ws[o]);
-        pv = bf16_to_f32(p_ws[o]);
+    // rows of this lane's output entries 16 eb + 4 g + i (-1: not attended)
+    int srow[2][4];
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = c0 + 16 * eb + 4 * g + i;
+        const int sv = e < top_k ? idx[(size_t)qi * top_k + e] : -1;
+        srow[eb][i] = (sv >= 0 && sv <= t) ? sv : -1;
       }
-      sds[e][h] = dsv * scale;
-      sp[e][h] = pv;
-    }
-    __syncthreads();
-    float acc[CH][NDJ];
+    v4f acc[BPW][2];
 #pragma unroll
-    for (int e = 0; e < CH; ++e)
+    for (int b = 0; b < BPW; ++b) acc[b][0] = acc[b][1] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NDJ; ++j) acc[e][j] = 0.f;
-#pragma unroll 1
-    for (int h = 0; h < H; ++h) {
-      float qd[NDJ], od[NDJ];
+    for (int part = 0; part < 2; ++part) {
+      const uint16_t* ws = part == 0 ? ds_ws : p_ws;
 #pragma unroll
-      for (int j = 0; j < NDJ; ++j) {
-        const int d = tid + DKV_NT * j;
-        qd[j] = d < DK ? bf16_to_f32(q[((size_t)qi * H + h) * DK + d]) : 0.f;
-        od[j] = d < DV ? bf16_to_f32(d_out[((size_t)qi * H + h) * DV + d]) : 0.f;
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks >= nks) break;
+        // A operands: entry 16 eb + n16, heads 32 ks + 8 g .. + 7
+        v8bf a[2];
+#pragma unroll
+        for (int eb = 0; eb < 2; ++eb) {
+          const int e = c0 + 16 * eb + n16;
+          const int h0 = 32 * ks + 8 * g;
+          v4i x = {0, 0, 0, 0};
+          if (e < top_k && h0 < H) {
+            const uint16_t* src = ws + ((size_t)qi * top_k + e) * H + h0;
+            if (heads8) {
+              x = *reinterpret_cast<const v4i*>(src);
+            } else {
+              uint16_t v[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[j] = h0 + j < H ? src[j] : (uint16_t)0;
+              __builtin_memcpy(&x, v, 16);
+            }
+          }
+          __builtin_memcpy(&a[eb], &x, 16);
+        }
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+          if (part == 1 && 16 * (blk0 + b) >= DV) continue;   // no V part past DV
+#pragma unroll
+          for (int eb = 0; eb < 2; ++eb)
+            acc[b][eb] = mfma16_bf16(a[eb], part == 0 ? bq[b][ks] : bo[b][ks], acc[b][eb]);
+        }
       }
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        const float a = sds[e][h], b = sp[e][h];
-#pragma unroll
-        for (int j = 0; j < NDJ; ++j) acc[e][j] = fmaf(a, qd[j], fmaf(b, od[j], acc[e][j]));
-      }
     }
+    // lane holds C[entry 16 eb + 4 g + i][dim 16 blk + n16]
 #pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const int sr = srow[e];
-      if (sr < 0) continue;
+    for (int b = 0; b < BPW; ++b) {
+      if (blk0 + b >= NBLK) continue;
+      const int d = 16 * (blk0 + b) + n16;
 #pragma unroll
-      for (int j = 0; j < NDJ; ++j) {
-        const int d = tid + DKV_NT * j;
-        if (d < DK) atomicAdd(&d_kv[(size_t)sr * DK + d], acc[e][j]);
-      }
+      for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (srow[eb][i] >= 0) atomicAdd(&d_kv[(size_t)srow[eb][i] * DK + d], acc[b][eb][i]);
     }
-    __syncthreads();
   }
 }
 
@@ -937,8 +983,9 @@ hipError_t launch_backward_shape(const MqaArgs& a, const float* lse_in, const ui
                      0, 1, a.n_kv, a.H, a.top_k, scale_log2, 1, a.top_k, nullptr, nullptr,
                      nullptr, nullptr, aux);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((mqa_dkv_kernel<DK, DV>), dim3(a.n_q), dim3(DKV_NT), 0, stream, a.q, d_out,
-                     a.idx, a.qpos_or_ctx, a.n_kv, a.H, a.top_k, a.scale, p_ws, ds_ws, dkv);
+  hipLaunchKernelGGL((mqa_dkv_kernel<DK, DV>), dim3(a.n_q, (DK / 16 + DKV_BLOCKS - 1) / DKV_BLOCKS),
+                     dim3(DKV_NT), 0, stream, a.q, d_out,
+                     a.idx, a.qpos_or_ctx, a.n_kv, a.H, a.top_k, p_ws, ds_ws, dkv);
   return hipGetLastError();
 }
 
