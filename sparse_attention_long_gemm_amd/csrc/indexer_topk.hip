@@ -5,21 +5,27 @@
 // Selection (same article, paragraph on fine-grained token selection): keep the top_k keys
 // under (score desc, position asc).
 //
-// Prefill kernel (one contiguous sequence)
+// Prefill kernel (one contiguous sequence, or several through a paged cache)
 //   One workgroup (8 waves) owns QB = 16 query rows and streams the keys 0..max(t) of its rows,
-//   128 keys per iteration, through a double-buffered LDS key tile (16-byte chunks
-//   XOR-swizzled).  Wave (hg, kh) holds the FP8 queries of indexer heads 16hg..16hg+15 for the
-//   16 rows in registers (the B operand of v_mfma_f32_16x16x128_f8f6f4, 8 VGPRs per head) and
-//   scores the 64 keys of tile half kh: the output lane owns one query row, so the head sum
-//   runs in registers.  ReLU is split as w ReLU(x) = (w x + w |x|) / 2: the |x| half costs one
-//   fma per product (the abs is a free operand modifier), and the linear half is a single
-//   product q_lin . k with q_lin[t] = sum_j w[t,j] q_I[t,j,:], run on bf16 MFMAs with q_lin
-//   split exactly into three bf16 pieces (FP8 keys convert to bf16 exactly).  The per-wave
-//   partial sums meet in LDS, where each wave applies the causal mask and a per-row threshold
-//   filter to its 2 rows and appends the surviving (score, position) items, in position order,
-//   to the row's candidate list in the workspace.  When lists near their capacity, every row
-//   past half of its slack is cut at the next iteration (all waves together) to a threshold
-//   that is at most its top_k-th score: from a per-row LDS histogram of the listed scores when
+//   128 keys per step, through a double-buffered LDS key tile (16-byte chunks XOR-swizzled).
+//   The waves have two roles; the two waves sharing a SIMD (w and w + 4) take one each.
+//   * Scorer wave hg (0..3) holds the FP8 queries of indexer heads 16hg..16hg+15 for the 16
+//     rows in registers (the B operand of v_mfma_f32_16x16x128_f8f6f4, 8 VGPRs per head) and
+//     scores all 128 keys of the tile: the output lane owns one query row, so the sum over its
+//     heads runs in registers.  ReLU is split as w ReLU(x) = (w x + w |x|) / 2: the |x| half
+//     costs one fma per product (the abs is a free operand modifier), and the linear half is
+//     a single product q_lin . k with q_lin[t] = sum_j w[t,j] q_I[t,j,:], run on bf16 MFMAs
+//     with q_lin split exactly into three bf16 pieces (FP8 keys convert to bf16 exactly);
+//     scorer hg computes it for 16-key fragments 2hg and 2hg+1, interleaved with its FP8
+//     MFMAs.  Scorers touch only LDS and registers.
+//   * Filter wave fw (0..3) owns rows 4fw..4fw+3: it issues the key-tile DMA, adds the four
+//     head-group partial sums and the linear term from LDS, applies the causal mask and a
+//     per-row threshold filter, and appends the surviving (score, position) items, in
+//     position order, to the row's candidate list in the workspace.  Its memory latencies sit
+//     beside the scorers' matrix work instead of in front of it.
+//   When lists near their capacity, every row past half of its slack is cut at the next step
+//   (all 8 waves, 2 rows each, with the rows' state passed through LDS) to a threshold that
+//   is at most its top_k-th score: from a per-row LDS histogram of the listed scores when
 //   that leaves enough room, else by an exact radix select (dsa_select.hpp).  Only keys
 //   scoring strictly above the row's threshold can enter afterwards (a later key with an equal
 //   score has a higher position, so it would lose the tie).  A last exact select per row
@@ -44,13 +50,17 @@ namespace dsa {
 namespace {
 
 constexpr int QB = 16;         // query rows per workgroup
-constexpr int NWAVE = 8;       // 4 head groups x 2 key-tile parities
+constexpr int NWAVE = 8;       // 4 scorer waves (head groups) + 4 filter waves
+constexpr int NSC = 4;         // scorer waves
+constexpr int NFW = NWAVE - NSC;   // filter waves
 constexpr int NT = NWAVE * kWave;
-constexpr int BK = 64;         // keys per tile; one iteration covers 2 tiles = 128 keys
-constexpr int BK2 = 2 * BK;
-constexpr int HPW = 16;        // indexer heads per wave
-constexpr int PSTR = BK + 4;   // padded LDS row stride (floats) of the partial scores
-constexpr int RPW = QB / NWAVE;  // query rows owned by each wave (filter + selection)
+constexpr int BK = 64;         // keys per filter lane pass (one key per lane)
+constexpr int BK2 = 2 * BK;    // keys per step (one key tile)
+constexpr int NFRAG = BK2 / 16;    // 16-key MFMA fragments per key tile
+constexpr int HPW = 16;        // indexer heads per scorer wave
+constexpr int PSTR = BK2 + 4;  // padded LDS row stride (floats) of the partial scores
+constexpr int RPF = QB / NFW;  // query rows owned by each filter wave
+constexpr int RPW = QB / NWAVE;  // rows each wave cuts and selects
 
 __device__ __forceinline__ v4i load16(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
 
@@ -83,15 +93,27 @@ struct CandItem {
   int32_t pos;
 };
 
+// A row's selection state, published by its filter wave for a cut step and the final select.
+struct RowState {
+  int cnt;      // listed candidates
+  float thr;    // strict threshold of the filter
+  u32 hi;       // largest listed order key
+  u32 lo;       // row histogram: range start, bin width (log2), valid
+  int shift;
+  int valid;
+  int t;        // last candidate position in the current segment (-1: none)
+};
+
 struct PrefillShared {
-  float part[2][2][4][QB][PSTR];  // [buffer][tile parity][head group][row][key]: sum w|x|
-  float plin[2][2][QB][PSTR];     // [buffer][tile parity][row][key]: sum w x (all heads)
+  float part[2][NSC][QB][PSTR];   // [buffer][head group][row][key]: sum w|x| of 16 heads
+  float plin[2][QB][PSTR];        // [buffer][row][key]: sum w x (all heads)
   alignas(16) uint8_t ktile[2][BK2 * 128];  // [buffer][key][128 B], 16 B chunks XOR-swizzled
   alignas(16) __bf16 qlin[3][4][kWave][8];  // [bf16 piece][k-step][lane][8]: B operand of
                                             // the linear term (stored element-wise)
   u32 hist[NWAVE][256];           // per-wave radix histograms
   u32 rhist[QB][256];             // per-row histogram of the listed scores (see RowHist)
-  int full[2][NWAVE];             // [iteration parity][wave]: a row of the wave is near full
+  RowState rs[QB];
+  int full[2][NFW];               // [step parity][filter wave]: a row of the wave is near full
   int seg_seq[QB];                // paged: each row's sequence until its segment ran, then -1
   int seg_t[QB];                  // paged: each row's last candidate position
 };
@@ -218,22 +240,6 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(int lo, int hi) {
   return r;
 }
 
-// Linear term sum_j w_j (q_j . k) = q_lin . k for one 16-key fragment and the 16 rows.
-// k-step ks of lane group g covers dims 16g + 8ks .. +8 (ks < 2) and 64 + 16g + 8(ks-2) .. +8,
-// the dims of the FP8 fragments.
-__device__ __forceinline__ v4f linear_term(const v8i& a, const PrefillShared& sh, int lane) {
-  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const v8bf ab = fp8x8_to_bf16(a[2 * ks], a[2 * ks + 1]);
-#pragma unroll
-    for (int pc = 0; pc < 3; ++pc)
-      acc[(3 * ks + pc) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          ab, *reinterpret_cast<const v8bf*>(&sh.qlin[pc][ks][lane][0]), acc[(3 * ks + pc) & 1], 0, 0, 0);
-  }
-  return acc[0] + acc[1];
-}
-
 // Key fragment (16 keys x 32 bytes per lane group) of tile row r0.. from the LDS key tile.
 __device__ __forceinline__ v8i frag_from_tile(const uint8_t* tile, int r, int g) {
   const v4i lo = *reinterpret_cast<const v4i*>(tile + r * 128 + 16 * kchunk(r, g));
@@ -269,13 +275,11 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   __shared__ PrefillShared sh;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
-  const int hg = wave & 3;       // head group: heads 16hg..16hg+15
-  const int kh = wave >> 2;      // key-tile parity: tile 2i+kh of iteration i
+  const bool scorer = wave < NSC;
   const int lane = tid & (kWave - 1);
   const int g = lane >> 4;       // lane group: 16-byte chunks g, g+4 of a row; output rows 4g..4g+3
   const int c16 = lane & 15;     // output column = query row within the block
   const int q0 = blockIdx.x * QB;
-  const bool heads_here = HPW * hg < H_I;
 
   // ---- last candidate position t of each row (clamped to the keys; -1: nothing) and the
   // sequence whose keys it reads (-1 for a row with nothing to score) ----
@@ -295,18 +299,6 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       }
     }
     if (t_lane < 0) seq_lane = -1;
-  }
-  // rows owned by this wave, their state (wave-uniform); t_own is set per sequence segment
-  int t_own[RPW], cnt[RPW];
-  float thr[RPW];
-  u32 hi_seen[RPW];   // per lane: largest order key this lane ever listed for the row
-  RowHist rowh[RPW];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    t_own[rr] = -1;
-    cnt[rr] = 0;
-    thr[rr] = -__builtin_inff();
-    hi_seen[rr] = 0u;
   }
 
   // ---- q_lin[row][d] = sum_j w[row][j] q_I[row][j][d] in fp32, split into 3 bf16 pieces
@@ -343,264 +335,352 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       }
     }
   }
-
-  // ---- queries of this wave's 16 heads for the 16 rows (MFMA B operand) ----
-  v8i qf[HPW];
-  float wv[HPW];
-  {
-    const int q = q0 + c16;
-#pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int h = hg * HPW + j;
-      const bool ok = (q < n_q) && (h < H_I);
-      qf[j] = load_row32(q_idx + ((size_t)q * H_I + h) * d_I, g, d_I, ok);
-      wv[j] = ok ? w[(size_t)q * H_I + h] : 0.f;
-    }
-  }
-
-  // ---- key tiles straight from global memory into LDS (global_load_lds, 16 bytes per lane):
-  // wave-load j (0..15) of a tile fills bytes [1024 j, 1024 j + 1024), i.e. rows 8j .. 8j+7;
-  // lane L fills physical chunk L % 8 of row 8j + L / 8, which holds logical chunk
-  // (L % 8) ^ ((row >> 1) & 7) (the kchunk swizzle).  Wave w issues wave-loads w and w + 8,
-  // whose rows have the same (row >> 1) & 7 pattern.  Keys past n_keys and chunks past d_I
-  // are not loaded: the tiles are zeroed once, so chunks past d_I stay zero, and a key past
-  // n_keys (whose slot may hold an older key) is past every row's last position t. ----
-  // Paged keys: wave-load j's 8 rows lie in one page; the wave looks the page up (a scalar
-  // load), and a page-table entry outside [0, n_pages) fills its LDS slots with zero keys
-  // instead.  Rows past the page table are not loaded (past every row's t).
-  const int dl_row = lane >> 3;
-  const int dl_chunk = (lane & 7) ^ ((4 * (wave & 1) + (dl_row >> 1)) & 7);
-  const bool dl_chunk_ok = 16 * dl_chunk < d_I;
-  const u32 dl_off = (u32)(dl_row * d_I + 16 * dl_chunk);
-  const int32_t* seg_pt = page_table;   // page-table row of the sequence being streamed
-  auto dma_tile = [&](int it_, int b) {
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = __builtin_amdgcn_readfirstlane(wave) + NWAVE * jj;   // wave-uniform
-      const int s0 = __builtin_amdgcn_readfirstlane(it_ * BK2 + 8 * j);
-      const uint8_t* src = k_idx + (size_t)s0 * d_I;
-      bool rows_ok = true;
-      if (PAGED) {
-        const int pi = s0 >> page_shift;        // page_size = 2^page_shift
-        int page = pi < max_pages ? seg_pt[pi] : -1;
-        page = __builtin_amdgcn_readfirstlane(page);
-        const bool page_ok = page >= 0 && page < n_pages;
-        if (!page_ok) {
-          if (pi < max_pages && dl_chunk_ok)   // inside the table: a page of zero keys
-            *reinterpret_cast<v4i*>(sh.ktile[b] + 1024 * j + 16 * lane) = v4i{0, 0, 0, 0};
-          continue;
-        }
-        src = k_idx + (((size_t)page << page_shift) + (s0 & ((1 << page_shift) - 1))) * d_I;
-      } else {
-        rows_ok = s0 + dl_row < n_keys;
-      }
-      // 64-bit base in scalar registers: each half through readfirstlane (which returns a
-      // signed int), widened as unsigned so the low half is not sign-extended
-      const uint64_t bp = (uint64_t)(uintptr_t)src;
-      const uint64_t base =
-          ((uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)(bp >> 32)) << 32) |
-          (uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)bp);
-      const u32 lds = __builtin_amdgcn_readfirstlane(
-          (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(sh.ktile[b] + 1024 * j));
-      if (dl_chunk_ok && rows_ok) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-                     :
-                     : "v"(dl_off), "s"(lds), "s"(base)
-                     : "memory", "m0");
-#pragma clang diagnostic pop
-      }
-    }
-  };
-
   for (int i = tid; i < 2 * BK2 * 128 / 16; i += NT)
     reinterpret_cast<v4i*>(&sh.ktile[0][0])[i] = v4i{0, 0, 0, 0};
-  int n_iter = 0;   // key tiles of the current segment
+  if (PAGED && tid < QB) {
+    sh.seg_seq[tid] = seq_lane;   // lanes 0..15 of wave 0 hold rows 0..15 (c16 == tid)
+    sh.seg_t[tid] = t_lane;
+  }
+  __syncthreads();   // q_lin pieces, zeroed key tiles and the segment table are in place
 
-  // Scores of key tile `kt` (keys [128 kt, 128 kt + 128)) from key buffer kt%2 into partial
-  // buffer kt%2.
-  auto compute = [&](int kt) {
-    const int buf = kt & 1;
-    const uint8_t* tile = sh.ktile[buf] + kh * BK * 128;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const v8i a = frag_from_tile(tile, 16 * f + c16, g);
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      if (heads_here) {
-        // software-pipelined: the epilogue of MFMA j follows the issue of MFMA j+2, so a
-        // lone wave does not stall on each result (about 0.7 of the matrix rate with the
-        // epilogue one MFMA behind, 0.8 with it two behind, measured); the barrier keeps the
-        // compiler from pulling the epilogues earlier
-        constexpr int PD = 3;
-        v4f x[PD + 1];
-#pragma unroll
-        for (int j = 0; j < HPW + PD; ++j) {
-          if (j < HPW) x[j % (PD + 1)] = mfma_fp8(a, qf[j]);
-          if (j >= PD) epi_abs(acc, x[(j - PD) % (PD + 1)], wv[j - PD]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+  // ---- the segments: the rows of one sequence at a time (contiguous keys: one segment).
+  // Every wave walks the same segments (read from LDS), so all waves meet the same barriers.
+  // run(t_act, t_max): t_act is row c16's last position in this segment (-1: not in it).
+  const int32_t* seg_pt = page_table;   // page-table row of the sequence being streamed
+  auto segments = [&](auto&& run) __attribute__((always_inline)) {
+    if constexpr (!PAGED) {
+      int t_max = t_lane;
+      for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
+      run(t_lane, t_max);
+    } else {
+#pragma unroll 1
+      for (;;) {
+        const int pend = sh.seg_seq[c16];
+        const uint64_t left = wave_ballot(pend >= 0) & 0xffffull;   // lanes 0..15: the 16 rows
+        if (left == 0ull) break;
+        const int cur = __shfl(pend, __builtin_ctzll(left));
+        const bool act = pend == cur;
+        const int t_act = act ? sh.seg_t[c16] : -1;
+        int t_max = t_act;
+        for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
+        seg_pt = page_table + (size_t)cur * max_pages;
+        __syncthreads();              // every wave has read seg_seq before it changes
+        if (tid < QB && act) sh.seg_seq[tid] = -1;
+        run(t_act, t_max);            // (its barriers publish the change)
       }
-      *reinterpret_cast<v4f*>(&sh.part[buf][kh][hg][c16][16 * f + 4 * g]) =
-          v4f{acc[0], acc[1], acc[2], acc[3]};
-      // linear term of fragment hg of this wave's tile (all heads at once)
-      if (f == hg)
-        *reinterpret_cast<v4f*>(&sh.plin[buf][kh][c16][16 * f + 4 * g]) = linear_term(a, sh, lane);
     }
   };
 
-  // This wave's rows over key tile `kt`: I = (sum_j w_j x_j + sum_j w_j |x_j|) / 2 =
-  // sum_j w_j ReLU(x_j); causal mask, threshold filter, ordered append.  All LDS reads are
-  // issued first.  Rows that could overflow in the next filter are flagged in full[kt % 2].
-  auto filter = [&](int kt) {
-    const int buf = kt & 1;
-    float scv[RPW][2];
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int r = RPW * wave + rr;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const float ab = ((sh.part[buf][half][0][r][lane] + sh.part[buf][half][1][r][lane]) +
-                          sh.part[buf][half][2][r][lane]) + sh.part[buf][half][3][r][lane];
-        scv[rr][half] = 0.5f * (sh.plin[buf][half][r][lane] + ab);
-      }
-    }
-    bool ps[RPW][2];
-    uint64_t mk[RPW][2];
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int t = t_own[rr];
-      const bool live = q0 + RPW * wave + rr < n_q && kt * BK2 <= t;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        ps[rr][half] = live && (kt * BK2 + half * BK + lane <= t) && (scv[rr][half] > thr[rr]);
-        mk[rr][half] = wave_ballot(ps[rr][half]);
-      }
-    }
-#pragma unroll
+  // ---- cut step (every wave, between two barriers): a filter wave flagged a row that could
+  // overflow in the next filter, so every row past half of its slack is cut.  The filter waves
+  // publish their rows' state, each wave cuts RPW rows, the filter waves take the new state
+  // back.  kf = the key tile the coming filter reads (a row whose keys end before it is done).
+  auto cut_rows = [&](int kf) __attribute__((always_inline)) {
+#pragma unroll 1
     for (int rr = 0; rr < RPW; ++rr) {
       const int r = RPW * wave + rr;
       const int q = q0 + r;
-      const int c0 = __builtin_popcountll(mk[rr][0]);
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (ps[rr][half]) {
-          const float sc = scv[rr][half];
-          const u32 key = ord_key(sc);
-          hi_seen[rr] = max(hi_seen[rr], key);
-          const int p = cnt[rr] + (half ? c0 : 0) + lanes_below(mk[rr][half]);
-          cand_score[(size_t)q * cap + p] = (sc == 0.f) ? 0.f : sc;
-          cand_pos[(size_t)q * cap + p] = kt * BK2 + half * BK + lane;
-          if (rowh[rr].valid) atomicAdd(&sh.rhist[r][hbin(key, rowh[rr])], 1u);
-        }
+      const RowState s = sh.rs[r];
+      if (q >= n_q || kf * BK2 > s.t || 2 * s.cnt <= top_k + cap) continue;
+      RowHist h;
+      h.lo = s.lo;
+      h.shift = s.shift;
+      h.valid = s.valid != 0;
+      int kept;
+      const float thr = wave_cut(cand_score + (size_t)q * cap, cand_pos + (size_t)q * cap, s.cnt,
+                                 top_k, cap, s.hi, h, sh.rhist[r], sh.hist[wave], &kept);
+      if (lane == 0) {
+        sh.rs[r].cnt = kept;
+        sh.rs[r].thr = thr;
+        sh.rs[r].lo = h.lo;
+        sh.rs[r].shift = h.shift;
+        sh.rs[r].valid = h.valid ? 1 : 0;
       }
-      cnt[rr] += c0 + __builtin_popcountll(mk[rr][1]);
     }
-    bool full = false;
+  };
+  auto any_full = [&](int it) __attribute__((always_inline)) {
+    bool f = false;
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr)
-      full |= (q0 + RPW * wave + rr < n_q) && cnt[rr] + BK2 > cap && (kt + 1) * BK2 <= t_own[rr];
-    if (lane == 0) sh.full[buf][wave] = full ? 1 : 0;
+    for (int v = 0; v < NFW; ++v) f |= sh.full[(it - 1) & 1][v] != 0;
+    return f;
   };
 
-  // One segment: the rows whose t_own >= 0 stream the keys 0..t_max of one sequence.
-  auto run_segment = [&](int t_max) {
-  n_iter = (t_max + BK2) / BK2;   // key tiles covering keys 0..t_max
-  __syncthreads();                // the previous segment's last reads of both tiles are done
-  dma_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // Step `it` scores key tile it and filters key tile it-1 (scored in the previous step), then
-  // synchronizes.  The two waves that share a SIMD (waves w and w+4, opposite tile parities)
-  // take the two phases in opposite orders, so one wave's VALU-heavy filter runs beside the
-  // other wave's MFMA work.
-#pragma unroll 1
-  for (int it = 0; it <= n_iter; ++it) {
-    const int kf = it - 1;   // tile filtered in this step
-
-    // ---- cut candidate lists, all waves together (a cut stalls the whole workgroup at the
-    // next barrier, so cuts are batched): when any row ended the previous filter with less
-    // than one tile of room, every row past half of its slack is cut ----
-    if (kf >= 1) {
-      bool any_full = false;
+  if (scorer) {
+    // ================= scorer waves: head group hg, all 128 keys of each tile =================
+    const int hg = wave;
+    const bool heads_here = HPW * hg < H_I;
+    v8i qf[HPW];
+    float wv[HPW];
+    {
+      const int q = q0 + c16;
 #pragma unroll
-      for (int v = 0; v < NWAVE; ++v) any_full |= sh.full[(kf - 1) & 1][v] != 0;
-      if (any_full) {
-#pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-          const int q = q0 + RPW * wave + rr;
-          if (q >= n_q || kf * BK2 > t_own[rr] || 2 * cnt[rr] <= top_k + cap) continue;
-          int kept;
-          thr[rr] = wave_cut(cand_score + (size_t)q * cap, cand_pos + (size_t)q * cap, cnt[rr],
-                             top_k, cap, wave_max_u32(hi_seen[rr]), rowh[rr],
-                             sh.rhist[RPW * wave + rr], sh.hist[wave], &kept);
-          cnt[rr] = kept;
-        }
+      for (int j = 0; j < HPW; ++j) {
+        const int h = hg * HPW + j;
+        const bool ok = (q < n_q) && (h < H_I);
+        qf[j] = load_row32(q_idx + ((size_t)q * H_I + h) * d_I, g, d_I, ok);
+        wv[j] = ok ? w[(size_t)q * H_I + h] : 0.f;
       }
     }
-
-    // ---- the next key tile into the other key buffer (read in the previous step); it has
-    // landed by the end of this step ----
-    if (it + 1 < n_iter) dma_tile(it + 1, (it + 1) & 1);
-
+    // sum_{j in group} w_j |x_j| of key tile kt (buffer kt%2) into part[kt%2][hg], and the
+    // linear term q_lin . k (all heads) of fragments 2hg, 2hg+1 into plin[kt%2]: the wave
+    // scores those two fragments first, with the twelve bf16 MFMAs of each interleaved into
+    // its FP8 MFMAs.  The next fragment's keys are read from LDS while one is scored.
+    const int hg_s = __builtin_amdgcn_readfirstlane(hg);
+    auto frag_row = [&](int i) __attribute__((always_inline)) { return 16 * ((2 * hg_s + i) & (NFRAG - 1)) + c16; };
+    auto compute = [&](int kt) __attribute__((always_inline)) {
+      const int buf = kt & 1;
+      const uint8_t* tile = sh.ktile[buf];
+      v8i a_next = frag_from_tile(tile, frag_row(0), g);
+#pragma unroll
+      for (int i = 0; i < NFRAG; ++i) {
+        const int f = (2 * hg_s + i) & (NFRAG - 1);
+        const v8i a = a_next;
+        if (i + 1 < NFRAG) a_next = frag_from_tile(tile, frag_row(i + 1), g);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        constexpr int NL = 12;   // linear-term MFMAs of a fragment: 4 k-steps x 3 q_lin pieces
+        v4f la[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        v8bf ab;
+        constexpr int LA = 3;
+        v8bf qlb[LA];
+        if (i < 2) {
+#pragma unroll
+          for (int m = 0; m < LA; ++m) qlb[m] = *reinterpret_cast<const v8bf*>(&sh.qlin[m % 3][m / 3][lane][0]);
+        }
+        auto lin_step = [&](int m) __attribute__((always_inline)) {
+          if (m % 3 == 0) ab = fp8x8_to_bf16(a[2 * (m / 3)], a[2 * (m / 3) + 1]);
+          la[m & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, qlb[m % LA], la[m & 1], 0, 0, 0);
+          if (m + LA < NL) qlb[m % LA] = *reinterpret_cast<const v8bf*>(&sh.qlin[(m + LA) % 3][(m + LA) / 3][lane][0]);
+        };
+        if (heads_here) {
+          // software-pipelined: the epilogue of MFMA j follows the issue of MFMA j+3, so the
+          // wave does not stall on each result; the barrier keeps the compiler from pulling
+          // the epilogues earlier
+          constexpr int PD = 3;
+          v4f x[PD + 1];
+#pragma unroll
+          for (int j = 0; j < HPW + PD; ++j) {
+            if (j < HPW) x[j % (PD + 1)] = mfma_fp8(a, qf[j]);
+            if (j >= PD) epi_abs(acc, x[(j - PD) % (PD + 1)], wv[j - PD]);
+            if (i < 2 && j < NL) lin_step(j);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if (i < 2) {
+#pragma unroll
+          for (int m = 0; m < NL; ++m) lin_step(m);
+        }
+        *reinterpret_cast<v4f*>(&sh.part[buf][hg][c16][16 * f + 4 * g]) =
+            v4f{acc[0], acc[1], acc[2], acc[3]};
+        if (i < 2) *reinterpret_cast<v4f*>(&sh.plin[buf][c16][16 * f + 4 * g]) = la[0] + la[1];
+      }
+    };
+    segments([&](int t_act, int t_max) __attribute__((always_inline)) {
+      const int n_iter = (t_max + BK2) / BK2;   // key tiles covering keys 0..t_max
+      __syncthreads();                           // the previous segment is done with the tiles
+      __syncthreads();                           // key tile 0 has landed
 #pragma unroll 1
-    for (int ph = 0; ph < 2; ++ph) {
-      if (ph == kh) {
-        // the scoring phase issues ahead of the other wave's filter on the SIMD, which keeps
-        // the matrix pipe fed while the filter's VALU work fills the gaps
-        __builtin_amdgcn_s_setprio(1);
+      for (int it = 0; it <= n_iter; ++it) {
+        if (it >= 2 && any_full(it)) {
+          __syncthreads();                       // the filter waves' state is published
+          cut_rows(it - 1);
+          __syncthreads();                       // the new state is published
+        }
         if (it < n_iter) compute(it);
-        __builtin_amdgcn_s_setprio(0);
-      } else {
-        if (kf >= 0) filter(kf);
+        __syncthreads();
       }
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next key tile has landed
-    __syncthreads();
-  }
-  };
-
-  if constexpr (!PAGED) {
-    // contiguous keys: one segment, every row
-    int t_max = t_lane;
-    for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) t_own[rr] = __shfl(t_lane, RPW * wave + rr);
-    run_segment(t_max);
+    });
   } else {
-    // Segments: the rows of one sequence at a time (one segment unless the workgroup's rows
-    // span sequences).  The rows' pending sequences wait in LDS, not in registers.
-    if (tid < QB) {
-      sh.seg_seq[tid] = seq_lane;   // lanes 0..15 of wave 0 hold rows 0..15 (c16 == tid)
-      sh.seg_t[tid] = t_lane;
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (;;) {
-      const int pend = sh.seg_seq[c16];
-      const uint64_t left = wave_ballot(pend >= 0) & 0xffffull;   // lanes 0..15: the 16 rows
-      if (left == 0ull) break;
-      const int cur = __shfl(pend, __builtin_ctzll(left));
-      const bool act = pend == cur;
-      const int t_act = act ? sh.seg_t[c16] : -1;
-      int t_max = t_act;
-      for (int o = 1; o < 16; o <<= 1) t_max = max(t_max, __shfl_xor(t_max, o));
+    // ================= filter waves: rows RPF*fw.., the key-tile DMA =================
+    const int fw = wave - NSC;
+    int t_own[RPF], cnt[RPF];
+    float thr[RPF];
+    u32 hi_seen[RPF];   // per lane: largest order key this lane ever listed for the row
+    RowHist rowh[RPF];
 #pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) t_own[rr] = __shfl(t_act, RPW * wave + rr);
-      seg_pt = page_table + (size_t)cur * max_pages;
-      __syncthreads();              // every wave has read seg_seq before it changes
-      if (tid < QB && act) sh.seg_seq[tid] = -1;
-      run_segment(t_max);           // (its barriers publish the change)
+    for (int rr = 0; rr < RPF; ++rr) {
+      t_own[rr] = -1;
+      cnt[rr] = 0;
+      thr[rr] = -__builtin_inff();
+      hi_seen[rr] = 0u;
     }
-  }
 
-  // ---- final exact selection of this wave's rows ----
+    // ---- key tiles straight from global memory into LDS (global_load_lds, 16 bytes per
+    // lane): wave-load j (0..15) of a tile fills bytes [1024 j, 1024 j + 1024), i.e. rows
+    // 8j .. 8j+7; lane L fills physical chunk L % 8 of row 8j + L / 8, which holds logical
+    // chunk (L % 8) ^ ((row >> 1) & 7) (the kchunk swizzle).  Filter wave fw issues wave-loads
+    // fw, fw + 4, fw + 8, fw + 12, whose rows have the same (row >> 1) & 7 pattern.  Keys past
+    // n_keys and chunks past d_I are not loaded: the tiles were zeroed, so chunks past d_I stay
+    // zero, and a key past n_keys (whose slot may hold an older key) is past every row's t.
+    // Paged keys: wave-load j's 8 rows lie in one page; the wave looks the page up (a scalar
+    // load), and a page-table entry outside [0, n_pages) fills its LDS slots with zero keys
+    // instead.  Rows past the page table are not loaded (past every row's t). ----
+    const int dl_row = lane >> 3;
+    const int dl_chunk = (lane & 7) ^ ((4 * (fw & 1) + (dl_row >> 1)) & 7);
+    const bool dl_chunk_ok = 16 * dl_chunk < d_I;
+    const u32 dl_off = (u32)(dl_row * d_I + 16 * dl_chunk);
+    auto dma_tile = [&](int it_, int b) __attribute__((always_inline)) {
 #pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = __builtin_amdgcn_readfirstlane(fw) + NFW * jj;   // wave-uniform
+        const int s0 = __builtin_amdgcn_readfirstlane(it_ * BK2 + 8 * j);
+        const uint8_t* src = k_idx + (size_t)s0 * d_I;
+        bool rows_ok = true;
+        if (PAGED) {
+          const int pi = s0 >> page_shift;        // page_size = 2^page_shift
+          int page = pi < max_pages ? seg_pt[pi] : -1;
+          page = __builtin_amdgcn_readfirstlane(page);
+          const bool page_ok = page >= 0 && page < n_pages;
+          if (!page_ok) {
+            if (pi < max_pages && dl_chunk_ok)   // inside the table: a page of zero keys
+              *reinterpret_cast<v4i*>(sh.ktile[b] + 1024 * j + 16 * lane) = v4i{0, 0, 0, 0};
+            continue;
+          }
+          src = k_idx + (((size_t)page << page_shift) + (s0 & ((1 << page_shift) - 1))) * d_I;
+        } else {
+          rows_ok = s0 + dl_row < n_keys;
+        }
+        // 64-bit base in scalar registers: each half through readfirstlane (which returns a
+        // signed int), widened as unsigned so the low half is not sign-extended
+        const uint64_t bp = (uint64_t)(uintptr_t)src;
+        const uint64_t base =
+            ((uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)(bp >> 32)) << 32) |
+            (uint64_t)(u32)__builtin_amdgcn_readfirstlane((u32)bp);
+        const u32 lds = __builtin_amdgcn_readfirstlane(
+            (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(sh.ktile[b] + 1024 * j));
+        if (dl_chunk_ok && rows_ok) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                       :
+                       : "v"(dl_off), "s"(lds), "s"(base)
+                       : "memory", "m0");
+#pragma clang diagnostic pop
+        }
+      }
+    };
+
+    // This wave's rows over key tile `kt`: I = (sum_j w_j x_j + sum_j w_j |x_j|) / 2 =
+    // sum_j w_j ReLU(x_j); causal mask, threshold filter, ordered append.  All LDS reads are
+    // issued first.  Rows that could overflow in the next filter are flagged in
+    // full[(kt + 1) % 2] (read at the start of the next step).
+    auto filter = [&](int kt) __attribute__((always_inline)) {
+      const int buf = kt & 1;
+      float scv[RPF][2];
+#pragma unroll
+      for (int rr = 0; rr < RPF; ++rr) {
+        const int r = RPF * fw + rr;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int k = BK * half + lane;
+          const float ab = ((sh.part[buf][0][r][k] + sh.part[buf][1][r][k]) +
+                            sh.part[buf][2][r][k]) + sh.part[buf][3][r][k];
+          scv[rr][half] = 0.5f * (sh.plin[buf][r][k] + ab);
+        }
+      }
+      bool ps[RPF][2];
+      uint64_t mk[RPF][2];
+#pragma unroll
+      for (int rr = 0; rr < RPF; ++rr) {
+        const int t = t_own[rr];
+        const bool live = q0 + RPF * fw + rr < n_q && kt * BK2 <= t;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          ps[rr][half] = live && (kt * BK2 + half * BK + lane <= t) && (scv[rr][half] > thr[rr]);
+          mk[rr][half] = wave_ballot(ps[rr][half]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPF; ++rr) {
+        const int r = RPF * fw + rr;
+        const int q = q0 + r;
+        const int c0 = __builtin_popcountll(mk[rr][0]);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          if (ps[rr][half]) {
+            const float sc = scv[rr][half];
+            const u32 key = ord_key(sc);
+            hi_seen[rr] = max(hi_seen[rr], key);
+            const int p = cnt[rr] + (half ? c0 : 0) + lanes_below(mk[rr][half]);
+            cand_score[(size_t)q * cap + p] = (sc == 0.f) ? 0.f : sc;
+            cand_pos[(size_t)q * cap + p] = kt * BK2 + half * BK + lane;
+            if (rowh[rr].valid) atomicAdd(&sh.rhist[r][hbin(key, rowh[rr])], 1u);
+          }
+        }
+        cnt[rr] += c0 + __builtin_popcountll(mk[rr][1]);
+      }
+      bool full = false;
+#pragma unroll
+      for (int rr = 0; rr < RPF; ++rr)
+        full |= (q0 + RPF * fw + rr < n_q) && cnt[rr] + BK2 > cap && (kt + 1) * BK2 <= t_own[rr];
+      if (lane == 0) sh.full[(kt + 1) & 1][fw] = full ? 1 : 0;
+    };
+
+    // the rows' state, for the cut step and the final selection
+    auto publish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int rr = 0; rr < RPF; ++rr) {
+        const u32 hi = wave_max_u32(hi_seen[rr]);
+        if (lane == 0) {
+          RowState& s = sh.rs[RPF * fw + rr];
+          s.cnt = cnt[rr];
+          s.thr = thr[rr];
+          s.hi = hi;
+          s.lo = rowh[rr].lo;
+          s.shift = rowh[rr].shift;
+          s.valid = rowh[rr].valid ? 1 : 0;
+          s.t = t_own[rr];
+        }
+      }
+    };
+    auto take_back = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int rr = 0; rr < RPF; ++rr) {
+        const RowState s = sh.rs[RPF * fw + rr];
+        cnt[rr] = s.cnt;
+        thr[rr] = s.thr;
+        rowh[rr].lo = s.lo;
+        rowh[rr].shift = s.shift;
+        rowh[rr].valid = s.valid != 0;
+      }
+    };
+
+    segments([&](int t_act, int t_max) __attribute__((always_inline)) {
+      const int n_iter = (t_max + BK2) / BK2;   // key tiles covering keys 0..t_max
+#pragma unroll
+      for (int rr = 0; rr < RPF; ++rr) t_own[rr] = __shfl(t_act, RPF * fw + rr);
+      __syncthreads();                           // the previous segment is done with the tiles
+      if (n_iter > 0) dma_tile(0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();                           // key tile 0 has landed
+#pragma unroll 1
+      for (int it = 0; it <= n_iter; ++it) {
+        if (it >= 2 && any_full(it)) {
+          publish();
+          __syncthreads();
+          cut_rows(it - 1);
+          __syncthreads();
+          take_back();
+        }
+        // Loads still pending from a cut are waited for first (vmcnt(0), nothing else): the
+        // compiler does not see the DMA, so a wait it placed after the DMA for one of those
+        // loads would also wait for the whole tile.
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        if (it + 1 < n_iter) dma_tile(it + 1, (it + 1) & 1);
+        if (it >= 1) filter(it - 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the next key tile has landed
+        __syncthreads();
+      }
+    });
+    publish();
+  }
+  __syncthreads();   // every row's final state is published
+
+  // ---- final exact selection, RPW rows per wave ----
+#pragma unroll 1
   for (int rr = 0; rr < RPW; ++rr) {
-    const int q = q0 + RPW * wave + rr;
+    const int r = RPW * wave + rr;
+    const int q = q0 + r;
     if (q >= n_q) continue;
-    const int n = cnt[rr];
+    const int n = sh.rs[r].cnt;
     int32_t* orow = out_idx + (size_t)q * top_k;
     const float* cs = cand_score + (size_t)q * cap;
     const int32_t* ci = cand_pos + (size_t)q * cap;
@@ -608,11 +688,11 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       for (int i = lane; i < top_k; i += kWave) orow[i] = (i < n) ? ci[i] : -1;
     } else {
       u32 T;
-      int r;
-      wave_radix_select_scores(cs, n, top_k, sh.hist[wave], T, r);
+      int r2;
+      wave_radix_select_scores(cs, n, top_k, sh.hist[wave], T, r2);
       wave_stable_keep(
           [&](int i) { CandItem it; it.score = cs[i]; it.pos = ci[i]; it.key = ord_key(it.score); return it; },
-          n, T, r, [&](const CandItem& it, int p) { if (p < top_k) orow[p] = it.pos; });
+          n, T, r2, [&](const CandItem& it, int p) { if (p < top_k) orow[p] = it.pos; });
     }
   }
 }
