@@ -335,6 +335,35 @@ def measured_ceilings(dsa, dev, reps: int = 3):
     return out
 
 
+def gather_ceilings(dsa, pre: Prefill, dev, reps: int = 3):
+    """Random-row gather rates on the attention's own rows: the prefill's KV pool and the
+    last 4096-row block's selected rows (4096 x 2048 rows of 1152 bytes, ascending positions),
+    moved by workgroups of 8 waves, one per CU, as in the attention: through the LDS DMA
+    (the attention's path) and through loads into registers; best of `reps` launches each."""
+    d = pre.inp
+    a, e = pre.blocks[-1]
+    idx = torch.empty((e - a, pre.top_k), dtype=torch.int32, device=dev)
+    dsa.indexer_topk(d["q_idx"][a:e], d["w"][a:e], d["k_idx"][:e], d["q_pos"][a:e], pre.top_k,
+                     out=idx, workspace=pre.ws)
+    n_wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
+    kv = d["kv"][:e]
+    out = {}
+    for kind, name in ((0, "gather_lds_dma_tbps"), (1, "gather_registers_tbps")):
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = _ev(), _ev()
+            e0.record()
+            nb = dsa.ceiling_gather(kind, kv, idx, n_wg, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, nb / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[name] = best
+    out["gather_kernel"] = ("dsa_ceiling_gather over the last block's index rows "
+                            f"({e - a} x {pre.top_k} rows of 1152 bytes), {n_wg} workgroups x 8 waves")
+    return out
+
+
 def cpu_baseline(prefill: Prefill, budget_s: float = 20.0):
     """The fp64 oracle (as it stands) on a strided sample of the 128K prefill's rows, timed on
     this host; extrapolated to all rows by the exact per-row work model."""
@@ -707,7 +736,13 @@ def main():
     if not args.no_extra:
         res["extra"] = extra_legs(pre, dec, dev, max(1, args.steps))
     ceil = measured_ceilings(dsa, dev)
+    ceil.update(gather_ceilings(dsa, pre, dev))
     res["ceilings"] = ceil
+    # the attention's row gathers: 1152 bytes per selected (t, s) pair
+    gathered = F_mqa / (2.0 * pre.wl.mqa.H * (pre.wl.mqa.D_k + pre.wl.mqa.D_v)) * (2 * pre.wl.mqa.D_k)
+    roof_mqa["gather"] = {"bytes": gathered, "achieved_tbps": gathered / t_mqa / 1e12,
+                          "frac_of_lds_dma_ceiling": gathered / t_mqa / 1e12
+                          / ceil["gather_lds_dma_tbps"]}
     roof_idx["frac_of_measured"] = roof_idx["achieved"] / ceil["fp8_mfma_tflops"]
     roof_mqa["frac_of_measured"] = roof_mqa["achieved"] / ceil["bf16_mfma_tflops"]
     decode["roofline"]["frac_of_measured"] = decode["roofline"]["achieved"] / ceil["hbm_read_gbps"]

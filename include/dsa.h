@@ -382,12 +382,22 @@ dsa_status dsa_sparse_mqa_decode_noalloc(const uint16_t* q, const uint16_t* kv_c
  * dsa_ceiling_read: streams `bytes` (a non-zero multiple of 16) from device memory `src` with
  *   16-byte non-temporal loads over n_wg workgroups of 256 threads; sink: device
  *   float[n_wg * 256], overwritten.
- * Both return DSA_ERR_INVALID_ARG for out-of-range arguments (nothing launched).
+ * dsa_ceiling_gather: gathers rows of `row_bytes` bytes (a multiple of 16, at most 2048) from
+ *   the device pool `pool` of n_rows rows along the index rows idx [n_q, top_k] int32 (device;
+ *   top_k a multiple of 32; an entry outside [0, n_rows) reads row 0), 32 listed rows at a
+ *   time by n_wg workgroups of 512 threads (8 waves, as the attention kernel): kind 0 moves
+ *   them with the LDS DMA (global_load_lds_dwordx4), kind 1 with 16-byte loads into
+ *   registers.  Bytes moved: n_q * top_k * row_bytes.  sink: device float[n_wg * 512],
+ *   overwritten.
+ * All return DSA_ERR_INVALID_ARG for out-of-range arguments (nothing launched).
  * ------------------------------------------------------------------------------------- */
 dsa_status dsa_ceiling_mfma(int32_t kind, int32_t n_wg, int32_t iters, float* sink,
                             double* flops, hipStream_t stream);
 dsa_status dsa_ceiling_read(const void* src, size_t bytes, int32_t n_wg, float* sink,
                             hipStream_t stream);
+dsa_status dsa_ceiling_gather(int32_t kind, const void* pool, int64_t n_rows, int32_t row_bytes,
+                              const int32_t* idx, int32_t n_q, int32_t top_k, int32_t n_wg,
+                              float* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

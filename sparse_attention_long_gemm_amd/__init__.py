@@ -61,6 +61,7 @@ SIGNATURES = {
                                                      _I, _I, _I, _F, _I, _P, _P, _P]),
     "dsa_ceiling_mfma": (ctypes.c_int, [_I, _I, _I, _P, _P, _P]),
     "dsa_ceiling_read": (ctypes.c_int, [_P, _Z, _I, _P, _P]),
+    "dsa_ceiling_gather": (ctypes.c_int, [_I, _P, ctypes.c_int64, _I, _P, _I, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -572,3 +573,20 @@ def ceiling_read(src: torch.Tensor, n_wg: int, sink: torch.Tensor) -> int:
     _check(load_library().dsa_ceiling_read(_ptr(src), nbytes, n_wg, _ptr(sink),
                                            _stream(sink.device)), "dsa_ceiling_read")
     return nbytes
+
+
+def ceiling_gather(kind: int, pool: torch.Tensor, idx: torch.Tensor, n_wg: int,
+                   sink: torch.Tensor) -> int:
+    """Launch the random-row gather ceiling kernel (kind 0: LDS DMA, kind 1: register loads)
+    over the rows of pool [n_rows, ...] listed in idx [n_q, top_k] int32, on the current
+    stream; returns the bytes gathered.  sink: float32 [n_wg * 512] on the GPU."""
+    _need(sink, "sink", (torch.float32,), 1)
+    _need(idx, "idx", (torch.int32,), 2)
+    if sink.numel() < n_wg * 512 or not pool.is_contiguous():
+        raise ValueError("sink too small or pool not contiguous")
+    row_bytes = pool[0].numel() * pool.element_size()
+    n_q, top_k = idx.shape
+    _check(load_library().dsa_ceiling_gather(kind, _ptr(pool), pool.shape[0], row_bytes,
+                                             _ptr(idx), n_q, top_k, n_wg, _ptr(sink),
+                                             _stream(sink.device)), "dsa_ceiling_gather")
+    return n_q * top_k * row_bytes

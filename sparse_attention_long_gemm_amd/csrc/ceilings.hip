@@ -63,6 +63,72 @@ __global__ __launch_bounds__(READ_NT) void ceiling_read_kernel(const v4i* __rest
   sink[(size_t)blockIdx.x * READ_NT + threadIdx.x] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
 }
 
+// Random-row gather along index rows, in the attention's shape: workgroups of 8 waves walk the
+// index rows blockIdx.x, blockIdx.x + gridDim.x, ...; each chunk of 32 listed rows is
+// row16 * 32 pieces of 16 bytes in row-major order, piece p loaded by thread p % 512.  An index
+// outside [0, n_rows) loads row 0.  KIND 0: LDS DMA (global_load_lds_dwordx4, one instruction
+// per wave-load with per-lane addresses) into two alternating 1 KB buffers per wave, at most
+// one wave-load of the wave in flight behind the newest; KIND 1: plain 16-byte loads into
+// registers, one chunk's loads of a thread in flight before they are folded into a checksum.
+constexpr int GATH_NT = 512;
+constexpr int GATH_CH = 32;
+constexpr int GATH_MAXPER = 8;   // pieces per thread and chunk (rows up to 2048 bytes)
+
+template <int KIND>
+__global__ __launch_bounds__(GATH_NT) void ceiling_gather_kernel(
+    const uint8_t* __restrict__ pool, int64_t n_rows, int row16, const int32_t* __restrict__ idx,
+    int n_q, int top_k, float* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[GATH_NT / kWave][2][kWave * 16];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid & (kWave - 1);
+  const int pieces = row16 * GATH_CH;
+  const int per = (pieces + GATH_NT - 1) / GATH_NT;
+  const size_t row_bytes = (size_t)row16 * 16;
+  v4i acc = {0, 0, 0, 0};
+  int n = 0;
+  for (int qr = blockIdx.x; qr < n_q; qr += gridDim.x) {
+    const int32_t* ir = idx + (size_t)qr * top_k;
+    for (int c = 0; c + GATH_CH <= top_k; c += GATH_CH) {
+      v4i x[GATH_MAXPER];
+#pragma unroll
+      for (int k = 0; k < GATH_MAXPER; ++k) {
+        if (k >= per) break;
+        const int p = tid + GATH_NT * k;
+        const int pp = p < pieces ? p : 0;
+        const int r = pp / row16, s = pp - r * row16;
+        const int64_t row = ir[c + r];
+        const uint8_t* src = pool + (size_t)(row >= 0 && row < n_rows ? row : 0) * row_bytes + 16 * s;
+        if constexpr (KIND == 0) {
+          const u32 lds = __builtin_amdgcn_readfirstlane(
+              (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(&buf[wave][n & 1][0]));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n\t"
+                       "s_waitcnt vmcnt(1)"
+                       :
+                       : "v"(src), "s"(lds)
+                       : "memory", "m0");
+#pragma clang diagnostic pop
+          ++n;
+        } else {
+          x[k] = *reinterpret_cast<const v4i*>(src);
+        }
+      }
+      if constexpr (KIND == 1) {
+#pragma unroll
+        for (int k = 0; k < GATH_MAXPER; ++k)
+          if (k < per) acc ^= x[k];
+      }
+    }
+  }
+  if constexpr (KIND == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    acc[0] = reinterpret_cast<const int*>(&buf[wave][0][0])[lane];
+  }
+  sink[(size_t)blockIdx.x * GATH_NT + tid] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -92,3 +158,21 @@ dsa_status dsa_ceiling_read(const void* src, size_t bytes, int32_t n_wg, float* 
 }
 
 }  // extern "C"
+
+extern "C" dsa_status dsa_ceiling_gather(int32_t kind, const void* pool, int64_t n_rows,
+                                         int32_t row_bytes, const int32_t* idx, int32_t n_q,
+                                         int32_t top_k, int32_t n_wg, float* sink,
+                                         hipStream_t stream) {
+  if ((kind != 0 && kind != 1) || !pool || !idx || !sink || n_rows < 1 || row_bytes < 16 ||
+      row_bytes % 16 != 0 || row_bytes / 16 * dsa::GATH_CH > dsa::GATH_MAXPER * dsa::GATH_NT ||
+      n_q < 1 || top_k < dsa::GATH_CH || top_k % dsa::GATH_CH != 0 || n_wg < 1)
+    return DSA_ERR_INVALID_ARG;
+  const auto* src = reinterpret_cast<const uint8_t*>(pool);
+  if (kind == 0)
+    hipLaunchKernelGGL(dsa::ceiling_gather_kernel<0>, dim3(n_wg), dim3(dsa::GATH_NT), 0, stream,
+                       src, n_rows, row_bytes / 16, idx, n_q, top_k, sink);
+  else
+    hipLaunchKernelGGL(dsa::ceiling_gather_kernel<1>, dim3(n_wg), dim3(dsa::GATH_NT), 0, stream,
+                       src, n_rows, row_bytes / 16, idx, n_q, top_k, sink);
+  return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}

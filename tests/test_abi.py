@@ -57,6 +57,15 @@ def test_ceiling_helpers_reject_bad_arguments():
     assert lib.dsa_ceiling_read(fake, 24, 1, fake, None) == -1
     assert lib.dsa_ceiling_read(fake, 0, 1, fake, None) == -1
     assert lib.dsa_ceiling_read(None, 32, 1, fake, None) == -1
+    # gather: kind, row size (multiple of 16, at most 2048 bytes), index rows of whole chunks
+    assert lib.dsa_ceiling_gather(2, fake, 10, 1152, fake, 1, 32, 1, fake, None) == -1
+    assert lib.dsa_ceiling_gather(0, fake, 10, 1160, fake, 1, 32, 1, fake, None) == -1
+    assert lib.dsa_ceiling_gather(0, fake, 10, 2064, fake, 1, 32, 1, fake, None) == -1
+    assert lib.dsa_ceiling_gather(0, fake, 10, 1152, fake, 1, 48, 1, fake, None) == -1
+    assert lib.dsa_ceiling_gather(0, fake, 10, 1152, fake, 1, 0, 1, fake, None) == -1
+    assert lib.dsa_ceiling_gather(0, fake, 0, 1152, fake, 1, 32, 1, fake, None) == -1
+    assert lib.dsa_ceiling_gather(1, fake, 10, 1152, None, 1, 32, 1, fake, None) == -1
+    assert lib.dsa_ceiling_gather(1, fake, 10, 1152, fake, 1, 32, 0, fake, None) == -1
 
 
 def test_workspace_sizes():
