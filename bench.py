@@ -52,6 +52,13 @@ def causal_pairs_range(q0, q1):
     return (q1 * (q1 + 1) - q0 * (q0 + 1)) // 2
 
 
+def scored_pairs_range(q0, q1, k):
+    """Sum over t in [q0, q1) with t + 1 > k of (t + 1): the (query, key) pairs whose scores
+    the selection depends on (a row with at most k candidates keeps all of them)."""
+    lo = max(q0, k)
+    return causal_pairs_range(lo, q1) if q1 > lo else 0
+
+
 def selected_pairs_range(q0, q1, k):
     return sum(min(k, t + 1) for t in range(q0, q1))
 
@@ -73,7 +80,8 @@ class Prefill:
                               dtype=torch.uint8, device=dev)
         self.nblk = (L + block - 1) // block
         self.blocks = [(b * block, min(L, (b + 1) * block)) for b in range(self.nblk)]
-        self.flops_idx = [2.0 * wl.idx.H_I * wl.idx.d_I * causal_pairs_range(a, e) for a, e in self.blocks]
+        self.flops_idx = [2.0 * wl.idx.H_I * wl.idx.d_I * scored_pairs_range(a, e, self.top_k)
+                          for a, e in self.blocks]
         self.flops_mqa = [2.0 * wl.mqa.H * (wl.mqa.D_k + wl.mqa.D_v) *
                           selected_pairs_range(a, e, self.top_k) for a, e in self.blocks]
         del d
@@ -124,7 +132,7 @@ class Decode:
         # are not counted.
         self.bytes_idx = sum(ix.d_I * c for c in ctx) + B * (ix.H_I * ix.d_I + ix.H_I * 4)
         self.bytes_mqa = sum(min(kk, c) for c in ctx) * m.D_k * 2 + B * m.H * (m.D_k + m.D_v) * 2
-        self.flops_idx = sum(2.0 * 64 * 128 * c for c in ctx)
+        self.flops_idx = sum(2.0 * 64 * 128 * c for c in ctx if c > kk)
         self.flops_mqa = sum(2.0 * m.H * (m.D_k + m.D_v) * min(kk, c) for c in ctx)
 
     def setup_append(self):
@@ -222,7 +230,7 @@ class Varlen:
                               device=dev)
         self.tokens = n_q
         ix, m = self.sp.idx, self.sp.mqa
-        self.flops_idx = sum(2.0 * ix.H_I * ix.d_I * causal_pairs_range(0, n) for n in lens)
+        self.flops_idx = sum(2.0 * ix.H_I * ix.d_I * scored_pairs_range(0, n, k) for n in lens)
         self.flops_mqa = sum(2.0 * m.H * (m.D_k + m.D_v) * selected_pairs_range(0, n, k)
                              for n in lens)
         self.lens = lens
@@ -689,7 +697,7 @@ def main():
                 "frac": F_idx / t_idx / PEAK_FP8,
                 "traffic": recorded_traffic("indexer_topk_prefill_kernel"),
                 "avg_launch_ms": t_idx / n_launch * 1e3,
-                "algorithmic": "2*H_I*d_I = 16384 FP8 flop per causal (t,s) pair; "
+                "algorithmic": "2*H_I*d_I = 16384 FP8 flop per causal (t,s) pair of rows with t+1 > top_k; "
                                f"{F_idx / n_launch:.4g} flop per launch on average"}
     roof_mqa = {"bound": "mfma", "kernel": "sparse_mqa_kernel<576,512>",
                 "achieved": F_mqa / t_mqa / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",

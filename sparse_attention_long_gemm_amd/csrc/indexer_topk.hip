@@ -302,6 +302,27 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     if (t_lane < 0) seq_lane = -1;
   }
 
+  // ---- rows with at most top_k candidates keep all of them whatever their scores: when that
+  // holds for every row of the block (the first top_k positions of each sequence), write
+  // positions 0..t in order, -1 padded, and score nothing.  Uniform over the workgroup: every
+  // wave reduces the same 16 row positions. ----
+  {
+    int t_all = t_lane;
+    for (int o = 1; o < 16; o <<= 1) t_all = max(t_all, __shfl_xor(t_all, o));
+    if (t_all < top_k) {
+#pragma unroll 1
+      for (int rr = 0; rr < RPW; ++rr) {
+        const int r = RPW * wave + rr;
+        const int t_r = __shfl(t_lane, r);   // lane r (c16 == r) holds row r's position
+        const int q = q0 + r;
+        if (q >= n_q) continue;
+        int32_t* orow = out_idx + (size_t)q * top_k;
+        for (int i = lane; i < top_k; i += kWave) orow[i] = i <= t_r ? i : -1;
+      }
+      return;
+    }
+  }
+
   // ---- q_lin[row][d] = sum_j w[row][j] q_I[row][j][d] in fp32, split into 3 bf16 pieces
   // (hi + mid + lo == q_lin exactly) laid out as the B operand of the linear-term MFMA ----
   {
