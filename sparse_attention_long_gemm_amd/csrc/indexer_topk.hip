@@ -724,7 +724,8 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 //
 //  1. dec_zero_kernel clears the per-row histograms and list counters.
 //  2. indexer_logits_paged_kernel (persistent, equal shares of all rows' keys per wave) writes
-//     the fp32 scores of keys [0, n) of each row (n = min(ctx, max_pages * page_size)) and
+//     the fp32 scores of keys [0, n) of each row with n > top_k (n = min(ctx, max_pages *
+//     page_size); a shorter row keeps all its keys and is not scored) and
 //     counts them in a per-row histogram of the top HBITS bits of their order keys (LDS
 //     histogram per wave, merged with atomics).
 //  3. dec_collect_kernel: the histogram gives the bin b1 that holds the top_k-th best score;
@@ -851,7 +852,8 @@ __global__ __launch_bounds__(SC_NT) void indexer_logits_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ ctx_lens, int B, int max_pages, int n_pages, FastDiv page,
-    int H_I, int d_I, int row_stride, float* __restrict__ logits, u32* __restrict__ hist) {
+    int H_I, int d_I, int row_stride, int top_k, float* __restrict__ logits,
+    u32* __restrict__ hist) {
   const int page_size = page.d;
   __shared__ u32 lh_all[SC_WAVES][NBIN / 2];   // two 16-bit bins per word
   __shared__ float stage_all[SC_WAVES][SC_STAGE * DEC_UNIT];   // scores waiting for a burst
@@ -865,8 +867,12 @@ __global__ __launch_bounds__(SC_NT) void indexer_logits_paged_kernel(
   u32* lh = lh_all[wave];
   const bool lo_ok = 16 * g < d_I, hi_ok = 16 * g + 64 < d_I;
 
-  // keys of row bb that are scored, and its unit count
-  auto row_len = [&](int bb) { return min(max(ctx_lens[bb], 0), row_stride); };
+  // keys of row bb that are scored: none when the row has at most top_k keys (it keeps them
+  // all whatever their scores; the selection writes positions 0..n-1 for it)
+  auto row_len = [&](int bb) {
+    const int n = min(max(ctx_lens[bb], 0), row_stride);
+    return n > top_k ? n : 0;
+  };
 
   // ---- this wave's unit range [u0, u1) of the flattened list, and the row / unit it starts in
   auto units = [&](int bb) -> long long {
@@ -1643,11 +1649,11 @@ hipError_t launch_indexer_topk_paged(const uint8_t* q_idx, const float* w, const
   if (page_size % DEC_UNIT == 0)
     hipLaunchKernelGGL(indexer_logits_paged_kernel<true>, grid, dim3(SC_NT), 0, stream, q_idx,
                        w, k_cache, page_table, ctx_lens, B, max_pages, n_pages, pdiv, H_I, d_I,
-                       row_stride, d.logits, d.hist);
+                       row_stride, top_k, d.logits, d.hist);
   else
     hipLaunchKernelGGL(indexer_logits_paged_kernel<false>, grid, dim3(SC_NT), 0, stream, q_idx,
                        w, k_cache, page_table, ctx_lens, B, max_pages, n_pages, pdiv, H_I, d_I,
-                       row_stride, d.logits, d.hist);
+                       row_stride, top_k, d.logits, d.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 cgrid((row_stride + COLLECT_CHUNK - 1) / COLLECT_CHUNK, B);
   hipLaunchKernelGGL(dec_collect_kernel, cgrid, dim3(SEL_NT), 0, stream, ctx_lens, row_stride,
