@@ -345,14 +345,13 @@ def measured_ceilings(dsa, dev, reps: int = 3):
 
 def gather_ceilings(dsa, pre: Prefill, dev, reps: int = 3):
     """Random-row gather rates on the attention's own rows: the prefill's KV pool and the
-    last 4096-row block's selected rows (4096 x 2048 rows of 1152 bytes, ascending positions),
+    last 4096-row block's selected rows (4096 x 2048 rows of 1152 bytes, ascending positions;
+    called after the timed steps, which leave that block's rows in pre.idx),
     moved by workgroups of 8 waves, one per CU, as in the attention: through the LDS DMA
     (the attention's path) and through loads into registers; best of `reps` launches each."""
     d = pre.inp
     a, e = pre.blocks[-1]
-    idx = torch.empty((e - a, pre.top_k), dtype=torch.int32, device=dev)
-    dsa.indexer_topk(d["q_idx"][a:e], d["w"][a:e], d["k_idx"][:e], d["q_pos"][a:e], pre.top_k,
-                     out=idx, workspace=pre.ws)
+    idx = pre.idx[: e - a]   # the last block's index rows, left there by the block loop
     n_wg = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
     kv = d["kv"][:e]
