@@ -91,6 +91,7 @@ __device__ __forceinline__ v4f mfma16_bf16(const v8bf& a, const v8bf& b, const v
 
 struct MqaShared {
   int rows[MAX_ROWS];   // physical row of each selected entry, or -1
+  int last[NW];         // per wave: the last entry that is a valid row, or -1
 };
 
 // Byte offset, inside its KV row, of the 16-byte slot that this lane fills in wave-load jj of
@@ -340,6 +341,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
       if (PAGED) pg[k] = ok ? page_table[(size_t)prow * max_pages + sv[k] / page_size] : -1;
       else pg[k] = ok ? 0 : -1;
     }
+    int last = -1;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int i = tid + k * NT;
@@ -351,7 +353,11 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
         row = sv[k];
       }
       sh.rows[i] = row;
+      if (row >= 0) last = i;
     }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) last = max(last, __shfl_xor(last, o));
+    if (lane == 0) sh.last[wave] = last;
   }
 
   v4f o[NDB];
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   float m_run = -__builtin_inff();   // per head (the 4 lanes of a head agree)
   float l_run = 0.f;                 // this lane's part of the head's sum
 
-  const int n_chunks = (nrows + CH - 1) / CH;
+  int n_chunks = (nrows + CH - 1) / CH;
   auto chunk_row = [&](int cc) -> int {
     const int e = cc * CH + c32;
     const int v = sh.rows[e < MAX_ROWS ? e : MAX_ROWS - 1];
@@ -374,6 +380,14 @@ __global__ __launch_bounds__(NT, 1) void sparse_mqa_kernel(
   gather_plan<DK>(wave, lane, slot_off);
   if (PROBS && tid < 2 * CH) psh[tid / CH][tid % CH] = 0.f;
   __syncthreads();   // rows[] complete
+  if constexpr (MODE == MODE_FWD) {
+    // chunks after the last valid entry (the -1 padding of a row with fewer than top_k keys)
+    // would add exactly nothing: they are not gathered or computed
+    int last = -1;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) last = max(last, sh.last[v]);
+    n_chunks = (last + CH) / CH;
+  }
   int row_nx = chunk_row(0);
   if (n_chunks > 0) gather_chunk<DK>(kt0, kv, row_nx, wave, lane, 0, GJ, slot_off);
   u32 vm_a = (u32)wave_ballot(row_nx >= 0);   // validity of the chunk being computed
