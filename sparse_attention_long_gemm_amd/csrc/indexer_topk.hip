@@ -540,6 +540,18 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     const bool dl_chunk_ok = 16 * dl_chunk < d_I;
     const u32 dl_off = (u32)(dl_row * d_I + 16 * dl_chunk);
     auto dma_tile = [&](int it_, int b) __attribute__((always_inline)) {
+      // the pages of this wave's four wave-loads, all read before the first key DMA: read
+      // between two DMAs, each page would wait for the DMA before it (one memory round trip
+      // per wave-load instead of one per tile)
+      int pg4[4];
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = __builtin_amdgcn_readfirstlane(fw) + NFW * jj;
+          const int pi = __builtin_amdgcn_readfirstlane(it_ * BK2 + 8 * j) >> page_shift;
+          pg4[jj] = pi < max_pages ? seg_pt[pi] : -1;
+        }
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = __builtin_amdgcn_readfirstlane(fw) + NFW * jj;   // wave-uniform
@@ -548,8 +560,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
         bool rows_ok = true;
         if (PAGED) {
           const int pi = s0 >> page_shift;        // page_size = 2^page_shift
-          int page = pi < max_pages ? seg_pt[pi] : -1;
-          page = __builtin_amdgcn_readfirstlane(page);
+          const int page = __builtin_amdgcn_readfirstlane(pg4[jj]);
           const bool page_ok = page >= 0 && page < n_pages;
           if (!page_ok) {
             if (pi < max_pages && dl_chunk_ok)   // inside the table: a page of zero keys
