@@ -965,6 +965,20 @@ __global__ __launch_bounds__(SC_NT) void indexer_logits_paged_kernel(
       gpage = live ? pt[pi < max_pages ? pi : max_pages - 1] : 0;
     }
     const u32 lds0 = (u32)(uintptr_t)(__attribute__((address_space(3))) void*)(ring_all[wave][nb]);
+    // unaligned pages: every wave-load's page entries are read before the first key DMA and
+    // unconditionally (a lane outside the row reads entry 0), so that waiting for them does not
+    // wait for the DMAs issued between them
+    int upg[DEC_UNIT_LOADS];
+    if constexpr (!ALIGNED) {
+#pragma unroll
+      for (int jj = 0; jj < DEC_UNIT_LOADS; ++jj) {
+        const int k = 8 * jj + (lane >> 3);
+        const int ch = (lane & 7) ^ ((k >> 1) & 7);
+        const int s = DEC_UNIT * c.j + k;
+        const bool in = live && s < c.n && 16 * ch < d_I;
+        upg[jj] = pt[fast_div(in ? s : 0, page)];
+      }
+    }
 #pragma unroll
     for (int jj = 0; jj < DEC_UNIT_LOADS; ++jj) {
       const int k = 8 * jj + (lane >> 3);
@@ -977,7 +991,7 @@ __global__ __launch_bounds__(SC_NT) void indexer_logits_paged_kernel(
         slot = gslot + k;
       } else {
         const int pi = fast_div(in ? s : 0, page);
-        pg = in ? pt[pi] : 0;
+        pg = in ? upg[jj] : 0;
         slot = s - pi * page_size;
       }
       const bool ok = in && pg >= 0 && pg < n_pages;
