@@ -198,10 +198,15 @@ def test_mqa_skips_invalid_entries_and_empty_rows():
     bad[70, 5] = -7
     bad[80, :] = -1             # nothing attended: o = 0, lse = -inf
     bad[90, 1] = 100000         # out of the kv range
+    # whole 32-entry chunks without a valid entry: in the middle of the list (still computed,
+    # valid entries follow), at its end (not gathered), and before the only valid chunk
+    bad[95, 32:64] = -1
+    bad[96, 41:] = -1
+    bad[97, :64] = -1
     step("mqa invalid entries")
     o, lse = run_mqa(d, bad.cuda())
     torch.cuda.synchronize()
-    rows = [50, 60, 70, 80, 90, 91]
+    rows = [50, 60, 70, 80, 90, 91, 95, 96, 97]
     _, o_ref, l_ref = orc.prefill(d, rows=rows, idx=bad[rows].numpy())
     check_attn(o[rows], lse[rows], o_ref, l_ref, "invalid")
     assert (o[80] == 0).all() and torch.isneginf(lse[80]).all()
