@@ -34,3 +34,13 @@ def test_source_digest_covers_every_listed_file():
         for f in files:
             assert os.path.isfile(os.path.join(bench.CSRC, f)), (kernel, f)
         assert len(bench.source_digest(kernel)) == 64
+
+
+def test_pair_counts_match_brute_force():
+    """Indexer work counts the causal pairs of rows with t + 1 > k (a row with at most k
+    candidates keeps them all); attention work counts min(k, t + 1) pairs per row."""
+    for q0, q1, k in [(0, 300, 64), (0, 64, 64), (10, 70, 64), (63, 65, 64), (500, 900, 2048),
+                      (2040, 2060, 2048), (0, 1, 1)]:
+        assert bench.causal_pairs_range(q0, q1) == sum(t + 1 for t in range(q0, q1))
+        assert bench.scored_pairs_range(q0, q1, k) == sum(t + 1 for t in range(q0, q1) if t + 1 > k)
+        assert bench.selected_pairs_range(q0, q1, k) == sum(min(k, t + 1) for t in range(q0, q1))
