@@ -99,6 +99,7 @@ struct RowState {
   int cnt;      // listed candidates
   float thr;    // strict threshold of the filter
   u32 hi;       // largest listed order key
+  u32 lo_seen;  // smallest order key ever listed (the list's smallest until its first cut)
   u32 lo;       // row histogram: range start, bin width (log2), valid
   int shift;
   int valid;
@@ -149,27 +150,57 @@ __device__ __forceinline__ u32 wave_max_u32(u32 v) {
   return v;
 }
 
+__device__ __forceinline__ u32 wave_min_u32(u32 v) {
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (u32)__shfl_xor((int)v, o));
+  return v;
+}
+
 // Cut a row's candidate list (n > top_k items in position order) in place.  Any threshold that
 // is at most the top_k-th best key seen so far is valid: a later key must beat it strictly to
 // enter (a later key with an equal score has a higher position, so it loses every tie).
-//  * Histogram cut (one pass): the lower edge T of the highest bin b whose suffix count reaches
-//    top_k; keeps every key >= T.  Used when the histogram is valid, b > 0 and the survivors
-//    leave room for two more iterations of appends.
-//  * Exact cut (radix select): keeps exactly the top_k; used otherwise (first cut, or scores
-//    piled into one bin, e.g. massive ties).
+//  * Histogram cut: the lower edge T of the highest bin b whose suffix count reaches top_k;
+//    keeps every key >= T.  The row's histogram serves (one pass); a row's first cut, which has
+//    none yet, counts the listed keys over their range [lo_seen, hi_seen] (tracked by the
+//    filter wave) in the wave's scratch histogram (one more pass).  Used when b > 0 and the
+//    survivors leave room for two more iterations of appends.
+//  * Exact cut (radix select): keeps exactly the top_k; used otherwise (scores piled into one
+//    bin, e.g. massive ties).
 // Both rebuild the row histogram over [T, hi_seen] from the survivors.  Returns the new
 // threshold score; *n_out receives the survivor count.
-__device__ float wave_cut(float* cs, int32_t* ci, int n, int top_k, int cap, u32 hi_seen,
-                          RowHist& h, u32* rh, u32* hist, int* n_out) {
+__device__ float wave_cut(float* cs, int32_t* ci, int n, int top_k, int cap, u32 lo_seen,
+                          u32 hi_seen, RowHist& h, u32* rh, u32* hist, int* n_out) {
   const int lane = threadIdx.x & (kWave - 1);
   u32 T = 0u;
   bool exact = true;
-  if (h.valid) {
+  // the histogram the threshold bin is chosen from: the row's own, or (first cut, when the
+  // row has none yet) one built here over the listed keys' range in this wave's scratch
+  RowHist hs = h;
+  const u32* hsrc = rh;
+  if (!h.valid) {
+    // before its first cut a row's list holds every key appended to it, so the smallest and
+    // largest listed keys are the ones its filter wave tracked
+    const ScoreKeys ld{cs, n};
+    hrange(hs, lo_seen, hi_seen);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int base = 0; base < n; base += kWave * kSelU) {
+      u32 kk[kSelU];
+      bool in[kSelU];
+      ld(base, kk, in);
+#pragma unroll
+      for (int u = 0; u < kSelU; ++u)
+        if (in[u]) atomicAdd(&hist[hbin(kk[u], hs)], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    hsrc = hist;
+  }
+  if (hs.valid) {
     u32 c[4];
     int tot = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      c[b] = rh[4 * lane + b];
+      c[b] = hsrc[4 * lane + b];
       tot += (int)c[b];
     }
     int incl = tot;  // suffix sum over lanes >= this lane
@@ -198,7 +229,7 @@ __device__ float wave_cut(float* cs, int32_t* ci, int n, int top_k, int cap, u32
     cnt_b = __builtin_amdgcn_readlane(cnt_b, src);
     if (who != 0ull && bsel > 0 && cnt_b <= cap - 2 * BK2) {
       exact = false;
-      T = h.lo + ((u32)bsel << h.shift);
+      T = hs.lo + ((u32)bsel << hs.shift);
     }
   }
   int r = 0;
@@ -410,7 +441,8 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       h.valid = s.valid != 0;
       int kept;
       const float thr = wave_cut(cand_score + (size_t)q * cap, cand_pos + (size_t)q * cap, s.cnt,
-                                 top_k, cap, s.hi, h, sh.rhist[r], sh.hist[wave], &kept);
+                                 top_k, cap, s.lo_seen, s.hi, h, sh.rhist[r], sh.hist[wave],
+                                 &kept);
       if (lane == 0) {
         sh.rs[r].cnt = kept;
         sh.rs[r].thr = thr;
@@ -516,6 +548,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     int t_own[RPF], cnt[RPF];
     float thr[RPF];
     u32 hi_seen[RPF];   // per lane: largest order key this lane ever listed for the row
+    u32 lo_seen[RPF];   // per lane: smallest order key this lane ever listed for the row
     RowHist rowh[RPF];
 #pragma unroll
     for (int rr = 0; rr < RPF; ++rr) {
@@ -523,6 +556,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
       cnt[rr] = 0;
       thr[rr] = -__builtin_inff();
       hi_seen[rr] = 0u;
+      lo_seen[rr] = 0xffffffffu;
     }
 
     // ---- key tiles straight from global memory into LDS (global_load_lds, 16 bytes per
@@ -632,6 +666,7 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
             const float sc = scv[rr][half];
             const u32 key = ord_key(sc);
             hi_seen[rr] = max(hi_seen[rr], key);
+            lo_seen[rr] = min(lo_seen[rr], key);
             const int p = cnt[rr] + (half ? c0 : 0) + lanes_below(mk[rr][half]);
             cand_score[(size_t)q * cap + p] = (sc == 0.f) ? 0.f : sc;
             cand_pos[(size_t)q * cap + p] = kt * BK2 + half * BK + lane;
@@ -652,11 +687,13 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
 #pragma unroll
       for (int rr = 0; rr < RPF; ++rr) {
         const u32 hi = wave_max_u32(hi_seen[rr]);
+        const u32 lo = wave_min_u32(lo_seen[rr]);
         if (lane == 0) {
           RowState& s = sh.rs[RPF * fw + rr];
           s.cnt = cnt[rr];
           s.thr = thr[rr];
           s.hi = hi;
+          s.lo_seen = lo;
           s.lo = rowh[rr].lo;
           s.shift = rowh[rr].shift;
           s.valid = rowh[rr].valid ? 1 : 0;
