@@ -643,37 +643,43 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
           scv[rr][half] = 0.5f * (sh.plin[buf][r][k] + ab);
         }
       }
-      bool ps[RPF][2];
-      uint64_t mk[RPF][2];
-#pragma unroll
-      for (int rr = 0; rr < RPF; ++rr) {
-        const int t = t_own[rr];
-        const bool live = q0 + RPF * fw + rr < n_q && kt * BK2 <= t;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          ps[rr][half] = live && (kt * BK2 + half * BK + lane <= t) && (scv[rr][half] > thr[rr]);
-          mk[rr][half] = wave_ballot(ps[rr][half]);
-        }
-      }
+      // Per row, one append pass covers both halves: a lane takes its first surviving key
+      // there, and a second pass (rare) takes the second half's key of lanes where both
+      // survive.  Each key's slot in the list is fixed by the ballots (position order), so
+      // the stores may go in any order.  The row's list is addressed from a scalar base with
+      // 32-bit lane offsets.
+      const int kb = kt * BK2;
 #pragma unroll
       for (int rr = 0; rr < RPF; ++rr) {
         const int r = RPF * fw + rr;
         const int q = q0 + r;
-        const int c0 = __builtin_popcountll(mk[rr][0]);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          if (ps[rr][half]) {
-            const float sc = scv[rr][half];
-            const u32 key = ord_key(sc);
-            hi_seen[rr] = max(hi_seen[rr], key);
-            lo_seen[rr] = min(lo_seen[rr], key);
-            const int p = cnt[rr] + (half ? c0 : 0) + lanes_below(mk[rr][half]);
-            cand_score[(size_t)q * cap + p] = (sc == 0.f) ? 0.f : sc;
-            cand_pos[(size_t)q * cap + p] = kt * BK2 + half * BK + lane;
-            if (rowh[rr].valid) atomicAdd(&sh.rhist[r][hbin(key, rowh[rr])], 1u);
-          }
+        const int t = t_own[rr];
+        if (q >= n_q || kb > t) continue;   // uniform
+        const bool p0 = (kb + lane <= t) && (scv[rr][0] > thr[rr]);
+        const bool p1 = (kb + BK + lane <= t) && (scv[rr][1] > thr[rr]);
+        const uint64_t m0 = wave_ballot(p0), m1 = wave_ballot(p1);
+        if ((m0 | m1) == 0ull) continue;    // uniform
+        const int c0 = __builtin_popcountll(m0);
+        const size_t rbase = (size_t)__builtin_amdgcn_readfirstlane(q) * cap;
+        char* srow = reinterpret_cast<char*>(cand_score + rbase);
+        char* prow = reinterpret_cast<char*>(cand_pos + rbase);
+        auto append = [&](float sc, int p, int pos) __attribute__((always_inline)) {
+          const u32 key = ord_key(sc);
+          hi_seen[rr] = max(hi_seen[rr], key);
+          lo_seen[rr] = min(lo_seen[rr], key);
+          const u32 off = 4u * (u32)p;
+          *reinterpret_cast<float*>(srow + off) = sc;
+          *reinterpret_cast<int32_t*>(prow + off) = pos;
+          if (rowh[rr].valid) atomicAdd(&sh.rhist[r][hbin(key, rowh[rr])], 1u);
+        };
+        if (p0 || p1) {
+          const int l0 = lanes_below(m0), l1 = c0 + lanes_below(m1);
+          append(p0 ? scv[rr][0] : scv[rr][1], cnt[rr] + (p0 ? l0 : l1), kb + (p0 ? 0 : BK) + lane);
         }
-        cnt[rr] += c0 + __builtin_popcountll(mk[rr][1]);
+        if ((m0 & m1) != 0ull) {            // uniform
+          if (p0 && p1) append(scv[rr][1], cnt[rr] + c0 + lanes_below(m1), kb + BK + lane);
+        }
+        cnt[rr] += c0 + __builtin_popcountll(m1);
       }
       bool full = false;
 #pragma unroll
