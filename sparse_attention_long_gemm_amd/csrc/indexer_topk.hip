@@ -155,6 +155,61 @@ __device__ __forceinline__ u32 wave_min_u32(u32 v) {
   return v;
 }
 
+// Keep, in place and in order, the listed items whose order key is > T (no ties to resolve):
+// the histogram cut.  Scores cs and positions ci of n items (rows 16-byte aligned) are read 4
+// consecutive items per lane with 16-byte loads (clamped to the last aligned quad, so no read
+// leaves the row's items), all 16 items of a lane in a batch before any is written; an item's
+// new slot is below its old one, so the writes never reach an unread item.  An item's slot is
+// the count of kept items before it: the kept items of lower lanes (one ballot per quad slot)
+// plus those earlier in its own quad.  emit(item, slot) writes it.  Returns the kept count.
+template <class Emit>
+__device__ int wave_keep_above(const float* cs, const int32_t* ci, int n, u32 T, Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int V = kSelU / 4;
+  const int last = (n - 1) & ~3;
+  int out = 0;
+  for (int base = 0; base < n; base += kWave * kSelU) {
+    v4f f[V];
+    v4i pq[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int i0 = min(base + 256 * v + 4 * lane, last);
+      f[v] = *reinterpret_cast<const v4f*>(cs + i0);
+      pq[v] = *reinterpret_cast<const v4i*>(ci + i0);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int i0 = base + 256 * v + 4 * lane;
+      u32 key[4];
+      bool keep[4];
+      uint64_t b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = ord_key(f[v][e]);
+        keep[e] = i0 + e < n && key[e] > T;
+        b[e] = wave_ballot(keep[e]);
+      }
+      int at = out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) at += lanes_below(b[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (keep[e]) {
+          CandItem it;
+          it.key = key[e];
+          it.score = f[v][e];
+          it.pos = pq[v][e];
+          emit(it, at);
+        }
+        at += keep[e] ? 1 : 0;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out += __builtin_popcountll(b[e]);
+    }
+  }
+  return out;
+}
+
 // Cut a row's candidate list (n > top_k items in position order) in place.  Any threshold that
 // is at most the top_k-th best key seen so far is valid: a later key must beat it strictly to
 // enter (a later key with an equal score has a higher position, so it loses every tie).
@@ -252,7 +307,7 @@ __device__ float wave_cut(float* cs, int32_t* ci, int n, int top_k, int cap, u32
     kept = wave_stable_keep(load, n, T, r, emit);
   } else {
     // keep every key >= T: "key > T - 1" with no ties to resolve (T >= 1 since bin b > 0)
-    kept = wave_stable_keep(load, n, T - 1u, 0, emit);
+    kept = wave_keep_above(cs, ci, n, T - 1u, emit);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   *n_out = kept;
