@@ -811,9 +811,9 @@ hipError_t launch_shape(const MqaArgs& a, hipStream_t stream) {
   const int rps = a.rows_per_split;
   // decode (one query per sequence, no sequence map): the selected rows come from a cache
   // far larger than L2 and the Infinity Cache and are read once per step, so they are
-  // gathered non-temporally (decode steps at batch 64 over contexts up to 128K about 7% faster
-  // in an A/B run; the same gathers in the 128K prefill, whose 151 MB pool the Infinity Cache
-  // holds, ran 10% slower)
+  // gathered non-temporally (decode steps at batch 64 over contexts up to 128K: 7% faster when
+  // the step follows a 512 MB write pass, unchanged when it follows the 128K prefill; the same
+  // gathers in that prefill, whose 151 MB pool the Infinity Cache holds, ran 10% slower)
   if (a.n_seq == 0)
     hipLaunchKernelGGL((sparse_mqa_kernel<DK, DV, true, false, MODE_FWD, true>),
                        dim3(a.n_q, a.n_split), dim3(NT), 0, stream, a.q, a.kv, a.idx,
