@@ -155,19 +155,21 @@ __device__ __forceinline__ u32 wave_min_u32(u32 v) {
   return v;
 }
 
-// Keep, in place and in order, the listed items whose order key is > T (no ties to resolve):
-// the histogram cut.  Scores cs and positions ci of n items (rows 16-byte aligned) are read 4
-// consecutive items per lane with 16-byte loads (clamped to the last aligned quad, so no read
-// leaves the row's items), all 16 items of a lane in a batch before any is written; an item's
-// new slot is below its old one, so the writes never reach an unread item.  An item's slot is
-// the count of kept items before it: the kept items of lower lanes (one ballot per quad slot)
-// plus those earlier in its own quad.  emit(item, slot) writes it.  Returns the kept count.
-template <class Emit>
-__device__ int wave_keep_above(const float* cs, const int32_t* ci, int n, u32 T, Emit emit) {
+// Keep, in place and in order, the listed items whose order key is > T, and (TIES) the first
+// r items equal to T in list order: the histogram cut (T one below a bin edge, no ties), the
+// exact cut and the final select.  Scores cs and positions ci of n items (rows 16-byte aligned)
+// are read 4 consecutive items per lane with 16-byte loads (clamped to the last aligned quad,
+// so no read leaves the row's items), all 16 items of a lane in a batch before any is written;
+// an item's new slot is below its old one, so the writes never reach an unread item.  An
+// item's slot (and a tied item's rank) counts the kept (tied) items before it: those of lower
+// lanes (one ballot per quad slot) and those earlier in its own quad.  emit(item, slot) writes
+// it.  Returns the kept count.
+template <bool TIES, class Emit>
+__device__ int wave_keep_quads(const float* cs, const int32_t* ci, int n, u32 T, int r, Emit emit) {
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int V = kSelU / 4;
   const int last = (n - 1) & ~3;
-  int out = 0;
+  int out = 0, ties = 0;
   for (int base = 0; base < n; base += kWave * kSelU) {
     v4f f[V];
     v4i pq[V];
@@ -187,8 +189,26 @@ __device__ int wave_keep_above(const float* cs, const int32_t* ci, int n, u32 T,
       for (int e = 0; e < 4; ++e) {
         key[e] = ord_key(f[v][e]);
         keep[e] = i0 + e < n && key[e] > T;
-        b[e] = wave_ballot(keep[e]);
       }
+      if constexpr (TIES) {
+        bool eq[4];
+        uint64_t beq[4];
+        int rank = ties;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          eq[e] = i0 + e < n && key[e] == T;
+          beq[e] = wave_ballot(eq[e]);
+          rank += lanes_below(beq[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          keep[e] = keep[e] || (eq[e] && rank < r);
+          rank += eq[e] ? 1 : 0;
+          ties += __builtin_popcountll(beq[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = wave_ballot(keep[e]);
       int at = out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) at += lanes_below(b[e]);
@@ -295,7 +315,6 @@ __device__ float wave_cut(float* cs, int32_t* ci, int n, int top_k, int cap, u32
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   hrange(h, T, hi_seen);
   int kept;
-  auto load = [&](int i) { CandItem it; it.score = cs[i]; it.pos = ci[i]; it.key = ord_key(it.score); return it; };
   auto emit = [&](const CandItem& it, int p) {
     if (p < cap) {
       cs[p] = it.score;
@@ -304,10 +323,10 @@ __device__ float wave_cut(float* cs, int32_t* ci, int n, int top_k, int cap, u32
     }
   };
   if (exact) {
-    kept = wave_stable_keep(load, n, T, r, emit);
+    kept = wave_keep_quads<true>(cs, ci, n, T, r, emit);
   } else {
     // keep every key >= T: "key > T - 1" with no ties to resolve (T >= 1 since bin b > 0)
-    kept = wave_keep_above(cs, ci, n, T - 1u, emit);
+    kept = wave_keep_quads<false>(cs, ci, n, T - 1u, 0, emit);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   *n_out = kept;
@@ -805,6 +824,80 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
   }
   __syncthreads();   // every row's final state is published
 
+  // The top_k-th key of a row whose list has a row histogram (it was cut at least once): the
+  // histogram (every listed key, over [lo, ...)) gives the bin holding it and the count of keys
+  // in higher bins; one pass over the list gathers that bin's keys into this wave's part of the
+  // score buffers (free now that scoring is done) and the exact select runs on those alone.
+  // Returns false (the caller selects over the whole list) when the row has no histogram or
+  // the bin does not fit.  T_out / r_out as for wave_radix_select.
+  constexpr int kSelBuf = (int)(sizeof(sh.part) / sizeof(u32)) / NWAVE;   // keys per wave
+  u32* const selbuf = reinterpret_cast<u32*>(&sh.part[0][0][0][0]) + wave * kSelBuf;
+  auto final_threshold_from_hist = [&](int r, const float* cs, int n, u32& T_out,
+                                       int& r_out) -> bool {
+    const RowState st = sh.rs[r];
+    if (st.valid == 0) return false;
+    RowHist h;
+    h.lo = st.lo;
+    h.shift = st.shift;
+    h.valid = true;
+    const u32* rh = sh.rhist[r];
+    u32 c[4];
+    int tot = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      c[b] = rh[4 * lane + b];
+      tot += (int)c[b];
+    }
+    int incl = tot;   // suffix sum over lanes >= this lane
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_down(incl, o);
+      if (lane + o < kWave) incl += t;
+    }
+    int bsel = -1, above = 0;
+    const int excl = incl - tot;
+    if (excl < top_k && top_k <= incl) {
+      int cum = excl;
+      for (int b = 3; b >= 0; --b) {
+        if (cum + (int)c[b] >= top_k) {
+          bsel = 4 * lane + b;
+          above = cum;
+          break;
+        }
+        cum += (int)c[b];
+      }
+    }
+    const uint64_t who = wave_ballot(bsel >= 0);
+    if (who == 0ull) return false;
+    const int src = __builtin_ctzll(who);
+    bsel = __builtin_amdgcn_readlane(bsel, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    const int nb = (int)rh[bsel];
+    if (nb > kSelBuf) return false;
+    // the keys of bin bsel, in any order
+    int m = 0;
+    const ScoreKeys ld{cs, n};
+    for (int base = 0; base < n; base += kWave * kSelU) {
+      u32 kk[kSelU];
+      bool in[kSelU];
+      ld(base, kk, in);
+#pragma unroll
+      for (int u = 0; u < kSelU; ++u) {
+        const bool hit = in[u] && hbin(kk[u], h) == bsel;
+        const uint64_t mm = wave_ballot(hit);
+        const int p = m + lanes_below(mm);
+        if (hit && p < kSelBuf) selbuf[p] = kk[u];
+        m += __builtin_popcountll(mm);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (m != nb) return false;   // (the histogram counts every listed key: not expected)
+    auto key_of = [&](int i) { return selbuf[i]; };
+    wave_radix_select_batched(ScalarKeys<decltype(key_of)>{key_of, m}, m, top_k - above,
+                              sh.hist[wave], T_out, r_out);
+    return true;
+  };
+
   // ---- final exact selection, RPW rows per wave ----
 #pragma unroll 1
   for (int rr = 0; rr < RPW; ++rr) {
@@ -820,10 +913,10 @@ __global__ __launch_bounds__(NT, 1) void indexer_topk_prefill_kernel(
     } else {
       u32 T;
       int r2;
-      wave_radix_select_scores(cs, n, top_k, sh.hist[wave], T, r2);
-      wave_stable_keep(
-          [&](int i) { CandItem it; it.score = cs[i]; it.pos = ci[i]; it.key = ord_key(it.score); return it; },
-          n, T, r2, [&](const CandItem& it, int p) { if (p < top_k) orow[p] = it.pos; });
+      if (!final_threshold_from_hist(r, cs, n, T, r2))
+        wave_radix_select_scores(cs, n, top_k, sh.hist[wave], T, r2);
+      wave_keep_quads<true>(cs, ci, n, T, r2,
+                            [&](const CandItem& it, int p) { if (p < top_k) orow[p] = it.pos; });
     }
   }
 }
