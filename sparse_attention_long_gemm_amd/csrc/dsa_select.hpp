@@ -10,7 +10,9 @@
 //      r of items with key == T that belong to the top-k (count(key > T) == k - r);
 //   2. a stable pass keeps every item with key > T and the first r items with key == T.
 //      Because items are stored in position order, "first r" is "lowest r positions", and
-//      the kept items come out in ascending position order.
+//      the kept items come out in ascending position order.  (The prefill indexer's keep pass,
+//      which reads 4 items per lane, sits beside its list cuts; the decode finish marks the
+//      kept positions in a bitmap.)
 #pragma once
 
 #include "dsa_common.hpp"
@@ -93,53 +95,6 @@ __device__ void block_radix_select(KeyOf key_of, int n, int k, SelectShared& sh,
   }
   T_out = prefix;
   r_out = remaining;
-}
-
-// Step 2.  load(i) returns an item with a `.key` field; emit(item, pos) stores a kept item at
-// output position pos.  In-place use (output aliasing the input) is safe: every item of a
-// chunk is loaded before any item of that chunk is stored, and stores go below the chunk end.
-// Returns the number of kept items (k when called with step 1's T and r).
-template <int NT, class Load, class Emit>
-__device__ int block_stable_keep(Load load, int n, u32 T, int r, Emit emit, SelectShared& sh) {
-  constexpr int NW = NT / kWave;
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  int ties = 0, out = 0;
-#pragma unroll 1
-  for (int base = 0; base < n; base += NT) {
-    const int i = base + tid;
-    const bool in = i < n;
-    auto item = load(in ? i : 0);
-    const bool gt = in && item.key > T;
-    const bool eq = in && item.key == T;
-    const uint64_t beq = wave_ballot(eq);
-    if ((tid & (kWave - 1)) == 0) sh.wave_a[wave] = __builtin_popcountll(beq);
-    __syncthreads();
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const int c = sh.wave_a[v];
-      before += (v < wave) ? c : 0;
-      tot += c;
-    }
-    const int rank = ties + before + lanes_below(beq);
-    const bool keep = gt || (eq && rank < r);
-    const uint64_t bk = wave_ballot(keep);
-    if ((tid & (kWave - 1)) == 0) sh.wave_b[wave] = __builtin_popcountll(bk);
-    __syncthreads();
-    int kbefore = 0, ktot = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const int c = sh.wave_b[v];
-      kbefore += (v < wave) ? c : 0;
-      ktot += c;
-    }
-    if (keep) emit(item, out + kbefore + lanes_below(bk));
-    ties += tot;
-    out += ktot;
-    __syncthreads();
-  }
-  return out;
 }
 
 }  // namespace dsa
@@ -287,48 +242,10 @@ __device__ void wave_radix_select_batched(const Loader& load, int n, int k, u32*
   r_out = remaining;
 }
 
-// Step 1 for one wave: the k-th largest order key T among items 0..n-1 (n > k >= 1) and the
-// number r of items equal to T that belong to the top k.  key_of(i) returns the ord_key of
-// item i.
-template <class KeyOf>
-__device__ void wave_radix_select(KeyOf key_of, int n, int k, u32* hist, u32& T_out, int& r_out) {
-  wave_radix_select_batched(ScalarKeys<KeyOf>{key_of, n}, n, k, hist, T_out, r_out);
-}
-
 // Step 1 over fp32 scores stored contiguously (see ScoreKeys).
 __device__ inline void wave_radix_select_scores(const float* cs, int n, int k, u32* hist,
                                                 u32& T_out, int& r_out) {
   wave_radix_select_batched(ScoreKeys{cs, n}, n, k, hist, T_out, r_out);
-}
-
-// Wave-level stable keep (see block_stable_keep).  All U chunks of a batch are loaded before
-// any item of the batch is emitted, and emits go below the batch end, so in-place use is safe.
-template <class Load, class Emit>
-__device__ int wave_stable_keep(Load load, int n, u32 T, int r, Emit emit) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int ties = 0, out = 0;
-  for (int base = 0; base < n; base += kWave * kSelU) {
-    decltype(load(0)) item[kSelU];
-#pragma unroll
-    for (int u = 0; u < kSelU; ++u) {
-      const int i = base + u * kWave + lane;
-      item[u] = load(i < n ? i : 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kSelU; ++u) {
-      const bool in = base + u * kWave + lane < n;
-      const bool gt = in && item[u].key > T;
-      const bool eq = in && item[u].key == T;
-      const uint64_t beq = wave_ballot(eq);
-      const int rank = ties + lanes_below(beq);
-      const bool keep = gt || (eq && rank < r);
-      const uint64_t bk = wave_ballot(keep);
-      if (keep) emit(item[u], out + lanes_below(bk));
-      ties += __builtin_popcountll(beq);
-      out += __builtin_popcountll(bk);
-    }
-  }
-  return out;
 }
 
 }  // namespace dsa
