@@ -71,8 +71,8 @@ def test_ceiling_helpers_reject_bad_arguments():
 def test_workspace_sizes():
     lib = dsa.load_library()
     # candidate lists of (score, position) pairs per row: room for top_k kept items plus two
-    # 128-key tiles of appends, at least 2*top_k + 128, rounded up to 128 entries
-    assert lib.dsa_indexer_topk_workspace_size(4096, 2048) == 4096 * 4224 * 8
+    # 128-key tiles of appends: 3*top_k + 128, at least top_k + 256, rounded up to 128 entries
+    assert lib.dsa_indexer_topk_workspace_size(4096, 2048) == 4096 * 6272 * 8
     assert lib.dsa_indexer_topk_workspace_size(16, 32) == 16 * 384 * 8
     assert lib.dsa_indexer_topk_workspace_size(-1, 32) == 0
     # paged: per key slot an fp32 score and a candidate (order key, position); per row a
