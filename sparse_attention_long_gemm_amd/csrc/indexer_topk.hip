@@ -970,7 +970,7 @@ __device__ __forceinline__ int hist_bin(u32 key) { return (int)(key >> (32 - HBI
 struct DecWs {
   float* logits;     // [B, row_stride]   scores
   u32* hist;         // [B, NBIN]         histogram of the scores' top HBITS order-key bits
-  int32_t* cnt;      // [B, 4]            list sizes: keys above bin b1, keys in b1
+  int32_t* cnt;      // [B, 4]            list sizes (keys above bin b1, keys in b1), b1, keys above b1
   int32_t* above;    // [B, kMaxK]        positions of the keys above bin b1
   u32* cand_key;     // [B, row_stride]   keys in bin b1: order key and position
   int32_t* cand_pos; // [B, row_stride]
@@ -1463,6 +1463,10 @@ __global__ __launch_bounds__(SEL_NT) void dec_collect_kernel(const int32_t* __re
   for (int u = 0; u < SEL_U; ++u) v[u] = row[min(base + u * SEL_NT + tid, n - 1)];
   int b1, above;
   threshold_bin<SEL_NT, NBIN>(ws.hist + (size_t)b * NBIN, top_k, sh_scan, b1, above);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {   // for the finish: the bin and the count above it
+    ws.cnt[4 * b + 2] = b1;
+    ws.cnt[4 * b + 3] = above;
+  }
   u32 key[SEL_U];
   int na = 0, nc = 0;
 #pragma unroll
@@ -1544,8 +1548,9 @@ __global__ __launch_bounds__(SEL_NT) void dec_finish_kernel(const int32_t* __res
     for (int i = tid; i < top_k; i += SEL_NT) orow[i] = (i < n) ? i : -1;
     return;
   }
-  int b1, above;
-  threshold_bin<SEL_NT, NBIN>(ws.hist + (size_t)b * NBIN, top_k, sh.scan, b1, above);
+  // the bin holding the top_k-th score and the count of keys above it, as the collect pass
+  // found them from the row's histogram
+  const int b1 = ws.cnt[4 * b + 2], above = ws.cnt[4 * b + 3];
   const int c = ws.cnt[4 * b + 1];                 // candidates in bin b1
   const bool use_bitmap = n <= SEL_BITMAP_WORDS * 32;
   const int n_words = (n + 31) / 32;
